@@ -1,0 +1,216 @@
+"""TurboQuant CPU oracle (fp64) -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It wraps ``tq_oracle.c`` (plain C, fp64,
+OpenMP over keys) through ctypes and shares no code with the GPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build() -> str:
+    """Compile the oracle with gcc (-O2, OpenMP). Returns the library path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-D_DEFAULT_SOURCE", "-Wall", "-shared", "-fPIC",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("m", ctypes.c_int), ("ng", ctypes.c_int),
+                ("gdim", ctypes.c_int * 2), ("gbits", ctypes.c_int * 2),
+                ("chan", ctypes.POINTER(ctypes.c_int))]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _p(a: np.ndarray, ct=ctypes.c_void_p):
+    return a.ctypes.data_as(ct)
+
+
+class Spec:
+    """Shape of one encoding: dimension d, sign-sketch rows m (0 = MSE-only),
+    channel groups [(d_g, b_g)] with b_g the codebook bits of group g, and the
+    channel list (group 0's channels then group 1's; None = identity)."""
+
+    def __init__(self, d: int, m: int, groups: Sequence[tuple], chan: Optional[np.ndarray] = None):
+        self.d, self.m = d, m
+        self.groups = [(int(a), int(b)) for a, b in groups]
+        self.chan = None if chan is None else np.ascontiguousarray(chan, dtype=np.int32)
+        c = _Cfg()
+        c.d, c.m, c.ng = d, m, len(self.groups)
+        for g, (dg, bg) in enumerate(self.groups):
+            c.gdim[g], c.gbits[g] = dg, bg
+        c.chan = _p(self.chan, ctypes.POINTER(ctypes.c_int)) if self.chan is not None else None
+        self._c = c
+
+    @property
+    def words(self) -> int:
+        return self.m // 32 + sum(b * (dg // 32) for dg, b in self.groups)
+
+    @property
+    def ng(self) -> int:
+        return len(self.groups)
+
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def codebook(bits: int):
+    """Lloyd-Max for N(0,1): (centroids[2^b], thresholds[2^b - 1], mse, iterations)."""
+    L = 1 << bits
+    c = np.zeros(L, np.float64)
+    t = np.zeros(max(L - 1, 1), np.float64)
+    mse = ctypes.c_double()
+    it = ctypes.c_int()
+    rc = lib().orc_codebook(bits, _p(c), _p(t), ctypes.byref(mse), ctypes.byref(it))
+    if rc:
+        raise ValueError(f"orc_codebook({bits}) -> {rc}")
+    return c, t[: L - 1], mse.value, it.value
+
+
+def rotation(gauss: np.ndarray) -> np.ndarray:
+    """Sign-fixed Householder Q of a square Gaussian matrix (fp64)."""
+    g = np.ascontiguousarray(gauss, dtype=np.float32)
+    d = g.shape[0]
+    out = np.zeros((d, d), np.float64)
+    if lib().orc_rotation(d, _p(g), _p(out)):
+        raise ValueError("orc_rotation")
+    return out
+
+
+class Params:
+    """The oracle's own parameters: rotations from its own QR, codebooks from its
+    own Lloyd-Max, the projection S as drawn (float32)."""
+
+    def __init__(self, spec: Spec, gaussians: Sequence[np.ndarray], proj: Optional[np.ndarray]):
+        self.spec = spec
+        self.rots = [rotation(g) for g in gaussians]
+        self.rot = np.ascontiguousarray(np.concatenate([r.ravel() for r in self.rots]))
+        m = spec.m
+        self.proj = np.ascontiguousarray(proj, dtype=np.float32) if m > 0 else np.zeros((1, spec.d), np.float32)
+        self.cent = np.zeros((2, 16), np.float64)
+        self.thr = np.zeros((2, 15), np.float32)
+        for g, (_, b) in enumerate(spec.groups):
+            c, t, _, _ = codebook(b)
+            self.cent[g, : len(c)] = c
+            self.thr[g, : len(t)] = t.astype(np.float32)
+
+
+def n_pad(n: int) -> int:
+    return 16 * ((n + 15) // 16)
+
+
+def encode(prm: Params, keys: np.ndarray):
+    """keys [n, d] float32 -> (bits [n_pad/16, W, 16] uint32, norms [n_pad, ng], rnorms [n_pad])."""
+    sp = prm.spec
+    k = np.ascontiguousarray(keys, dtype=np.float32)
+    n = k.shape[0]
+    npd = n_pad(n)
+    bits = np.zeros((npd // 16, sp.words, 16), np.uint32)
+    norms = np.zeros((npd, sp.ng), np.float32)
+    rnorms = np.zeros(npd, np.float32)
+    rc = lib().orc_encode(sp.ref(), _p(prm.rot), _p(prm.proj), _p(prm.cent), _p(prm.thr), _p(k),
+                          ctypes.c_long(n), _p(bits), _p(norms), _p(rnorms))
+    if rc:
+        raise ValueError("orc_encode")
+    return bits, norms, rnorms
+
+
+def decode(prm: Params, bits: np.ndarray, norms: np.ndarray, n: int) -> np.ndarray:
+    sp = prm.spec
+    out = np.zeros((n, sp.d), np.float64)
+    rc = lib().orc_decode(sp.ref(), _p(prm.rot), _p(prm.cent), _p(np.ascontiguousarray(bits, np.uint32)),
+                          _p(np.ascontiguousarray(norms, np.float32)), ctypes.c_long(n), _p(out))
+    if rc:
+        raise ValueError("orc_decode")
+    return out
+
+
+def unpack(spec: Spec, bits: np.ndarray, n: int):
+    codes = np.zeros((n, spec.d), np.int32)
+    signs = np.zeros((n, max(spec.m, 1)), np.uint8)
+    if lib().orc_unpack(spec.ref(), _p(np.ascontiguousarray(bits, np.uint32)), ctypes.c_long(n), _p(codes), _p(signs)):
+        raise ValueError("orc_unpack")
+    return codes, signs[:, : spec.m]
+
+
+def score(prm: Params, bits, norms, rnorms, n: int, q: np.ndarray) -> np.ndarray:
+    """Estimated inner products [G, n] (fp64) of queries q [G, d] against one bank."""
+    sp = prm.spec
+    qq = np.ascontiguousarray(q, dtype=np.float32)
+    G = qq.shape[0]
+    out = np.zeros((G, n), np.float64)
+    rc = lib().orc_score(sp.ref(), _p(prm.rot), _p(prm.proj), _p(prm.cent), _p(np.ascontiguousarray(bits, np.uint32)),
+                         _p(np.ascontiguousarray(norms, np.float32)), _p(np.ascontiguousarray(rnorms, np.float32)),
+                         ctypes.c_long(n), _p(qq), G, _p(out))
+    if rc:
+        raise ValueError("orc_score")
+    return out
+
+
+def score_pairs(prm: Params, bits, norms, rnorms, q: np.ndarray, qi: np.ndarray, ki: np.ndarray) -> np.ndarray:
+    sp = prm.spec
+    qq = np.ascontiguousarray(q, dtype=np.float32)
+    qi = np.ascontiguousarray(qi, dtype=np.int32)
+    ki = np.ascontiguousarray(ki, dtype=np.int64)
+    out = np.zeros(len(qi), np.float64)
+    rc = lib().orc_score_pairs(sp.ref(), _p(prm.rot), _p(prm.proj), _p(prm.cent),
+                               _p(np.ascontiguousarray(bits, np.uint32)), _p(np.ascontiguousarray(norms, np.float32)),
+                               _p(np.ascontiguousarray(rnorms, np.float32)), _p(qq), qq.shape[0], _p(qi), _p(ki),
+                               ctypes.c_long(len(qi)), _p(out))
+    if rc:
+        raise ValueError("orc_score_pairs")
+    return out
+
+
+def topk(scores: np.ndarray, k: int):
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    G, n = s.shape
+    vals = np.zeros((G, k), np.float64)
+    idx = np.zeros((G, k), np.int64)
+    if lib().orc_topk(_p(s), ctypes.c_long(n), G, k, _p(vals), _p(idx)):
+        raise ValueError("orc_topk")
+    return vals, idx
+
+
+def lloyd_empirical(points: np.ndarray, L: int, start: np.ndarray, weights: Optional[np.ndarray] = None,
+                    max_iter: int = 100000):
+    """Lloyd iteration on a weighted empirical set: (centroids, thresholds, mse, iterations)."""
+    pts = np.ascontiguousarray(points, dtype=np.float64)
+    w = None if weights is None else np.ascontiguousarray(weights, dtype=np.float64)
+    c = np.ascontiguousarray(start, dtype=np.float64).copy()
+    t = np.zeros(max(L - 1, 1), np.float64)
+    mse = ctypes.c_double()
+    it = lib().orc_lloyd_empirical(_p(pts), _p(w) if w is not None else None, ctypes.c_long(len(pts)), L, _p(c), _p(t),
+                                   ctypes.byref(mse), max_iter)
+    if it < 0:
+        raise ValueError("orc_lloyd_empirical")
+    return c, t[: L - 1], mse.value, it
+
+
+def bucketize(z: float, thresholds: np.ndarray) -> int:
+    t = np.ascontiguousarray(thresholds, dtype=np.float32)
+    lib().orc_bucketize.argtypes = [ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+    return lib().orc_bucketize(ctypes.c_float(z), _p(t), len(t) + 1)

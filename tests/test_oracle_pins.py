@@ -1,0 +1,469 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test here checks the oracle against something other than itself: closed
+forms, a textbook table, direct numerical minimisation, brute force on tiny
+inputs, the statistics the method guarantees (unbiasedness, the closed-form
+variance of the sign sketch, the 2/pi shrinkage of an MSE-only 1-bit
+quantiser), the 3-bit distortion the turboquant-pytorch write-up reports, and
+hand-built inputs whose encoding is known bit by bit.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, optimize, stats
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------
+# codebook (Lloyd-Max for N(0,1))
+# ------------------------------------------------------------------------------------
+
+def test_codebook_one_bit_closed_form():
+    c, t, mse, _ = oracle.codebook(1)
+    a = math.sqrt(2 / math.pi)  # E|X| for X ~ N(0,1)
+    np.testing.assert_allclose(c, [-a, a], rtol=0, atol=1e-14)
+    assert t[0] == 0.0
+    assert abs(mse - (1 - 2 / math.pi)) < 1e-14
+
+
+def _read_max_table():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "gaussian_lloyd_max_max1960.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        L, c, t, mse = [f.strip() for f in line.split("|")]
+        rows[int(L)] = ([float(v) for v in c.split()], [] if t == "-" else [float(v) for v in t.split()], float(mse))
+    return rows
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_textbook_table(bits):
+    L = 1 << bits
+    cpos, tpos, mse_tab = _read_max_table()[L]
+    c, t, mse, _ = oracle.codebook(bits)
+    np.testing.assert_allclose(c[L // 2:], cpos, atol=1.5e-3)
+    np.testing.assert_allclose(t[L // 2:], tpos, atol=1.5e-3)
+    assert abs(mse - mse_tab) / mse_tab < 0.05
+
+
+def _cond_mean(a, b):
+    m0 = integrate.quad(stats.norm.pdf, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+    m1 = integrate.quad(lambda x: x * stats.norm.pdf(x), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+    return m1 / m0
+
+
+def _mse_of_thresholds(tpos):
+    """MSE of the symmetric quantizer with positive thresholds tpos (0 is always a
+    threshold for an even level count), each cell represented by its conditional
+    mean; integrals by adaptive quadrature (no closed form)."""
+    edges = [0.0] + list(tpos) + [np.inf]
+    tot = 0.0
+    for a, b in zip(edges[:-1], edges[1:]):
+        c = _cond_mean(a, b)
+        tot += integrate.quad(lambda x: (x - c) ** 2 * stats.norm.pdf(x), a, b, epsabs=1e-14, epsrel=1e-12)[0]
+    return 2 * tot
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_is_the_direct_minimiser(bits):
+    """Minimise the quadrature MSE over the free thresholds directly (no Lloyd
+    iteration involved) and compare with the oracle's fixed point."""
+    L = 1 << bits
+    c, t, mse, _ = oracle.codebook(bits)
+    x0 = t[L // 2:] * (1 + 0.03 * np.linspace(-1, 1, L // 2 - 1))  # perturbed start
+    if L == 4:
+        r = optimize.minimize_scalar(lambda v: _mse_of_thresholds([v]), bounds=(0.5, 1.5), method="bounded",
+                                     options={"xatol": 1e-10})
+        tbest = np.array([r.x])
+    else:
+        r = optimize.minimize(lambda v: _mse_of_thresholds(np.sort(v)), x0, method="Nelder-Mead",
+                              options={"xatol": 1e-9, "fatol": 1e-15, "maxiter": 20000})
+        tbest = np.sort(r.x)
+    np.testing.assert_allclose(tbest, t[L // 2:], atol=2e-4)
+    assert abs(_mse_of_thresholds(tbest) - mse) < 1e-9
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_fixed_point_conditions(bits):
+    """Centroid = conditional mean of its cell (by quadrature); threshold = midpoint."""
+    L = 1 << bits
+    c, t, _, _ = oracle.codebook(bits)
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    for k in range(L):
+        assert abs(_cond_mean(edges[k], edges[k + 1]) - c[k]) < 1e-10
+    np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), atol=1e-15)
+    np.testing.assert_array_equal(c, -c[::-1])  # symmetric, middle threshold exactly 0
+
+
+def _brute_force_partition(x, L):
+    """Global optimum of the L-cell quantizer of a tiny sorted set: exhaustive
+    over contiguous partitions."""
+    n = len(x)
+    best = (np.inf, None)
+    for cuts in itertools.combinations(range(1, n), L - 1):
+        parts = np.split(x, cuts)
+        sse = sum(((p - p.mean()) ** 2).sum() for p in parts)
+        if sse < best[0]:
+            best = (sse, np.array([p.mean() for p in parts]))
+    return best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_lloyd_brute_force_tiny_sets(seed):
+    g = np.random.default_rng(seed)
+    n = int(g.integers(5, 11))
+    L = int(g.integers(2, 5))
+    x = np.sort(g.standard_normal(n) * g.uniform(0.5, 2.0))
+    sse, cents = _brute_force_partition(x, L)
+    # the optimum is a fixed point of the iteration
+    c, t, mse, it = oracle.lloyd_empirical(x, L, cents)
+    np.testing.assert_allclose(c, cents, atol=1e-12)
+    assert abs(mse - sse) < 1e-10
+    # from a generic start the iteration reaches a fixed point no better than the optimum
+    c2, t2, mse2, _ = oracle.lloyd_empirical(x, L, np.linspace(x[0], x[-1], L))
+    assert mse2 >= sse - 1e-10
+    for k in range(L):
+        lo = -np.inf if k == 0 else t2[k - 1]
+        hi = np.inf if k == L - 1 else t2[k]
+        cell = x[(x >= lo) & (x < hi)]
+        if len(cell):
+            assert abs(cell.mean() - c2[k]) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bucketize_is_nearest_centroid(bits):
+    """Thresholds are midpoints, so the bucket is the nearest centroid; exhaustive
+    over the float32 neighbours of every threshold, plus random draws."""
+    c, t, _, _ = oracle.codebook(bits)
+    tf = t.astype(np.float32)
+    zs = []
+    for tau in tf:
+        v = np.float32(tau)
+        zs.append(v)
+        up, dn = v, v
+        for _ in range(4):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(-np.inf))
+            zs += [up, dn]
+    zs += list(np.random.default_rng(0).standard_normal(2000).astype(np.float32) * 1.5)
+    for z in zs:
+        k = oracle.bucketize(float(z), tf)
+        if np.any(tf == z):   # exactly on a float32 threshold: ties go up
+            assert k == int(np.nonzero(tf == z)[0][0]) + 1
+        else:
+            dist = np.abs(float(z) - c)
+            order = np.argsort(dist)
+            if dist[order[1]] - dist[order[0]] > 1e-12:
+                assert k == int(order[0])
+            else:  # equidistant in fp64 arithmetic (z within ~1e-12 of a midpoint)
+                assert k in (int(order[0]), int(order[1]))
+
+
+# ------------------------------------------------------------------------------------
+# rotation
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [32, 96, 128, 768])
+def test_rotation_is_sign_fixed_q_factor(d):
+    G = np.random.default_rng(d).standard_normal((d, d)).astype(np.float32)
+    R = oracle.rotation(G)
+    assert np.abs(R @ R.T - np.eye(d)).max() < 1e-12
+    T = R.T @ G.astype(np.float64)          # the triangular factor
+    assert np.abs(np.tril(T, -1)).max() < 1e-10 * np.abs(T).max()
+    assert (np.diag(T) > 0).all()
+    # the same unique factor as a library QR with the signs fixed
+    Q, Rq = np.linalg.qr(G.astype(np.float64))
+    assert np.abs(Q * np.sign(np.diag(Rq)) - R).max() < 1e-10
+
+
+def _perm_upper(d, seed):
+    """G = P U with P a permutation (not an involution) and U upper triangular with a
+    positive diagonal: its sign-fixed Q factor is exactly P."""
+    g = np.random.default_rng(seed)
+    perm = np.roll(np.arange(d), 1 + seed % (d - 1))
+    P = np.eye(d)[perm]               # P[j, perm[j]] = 1
+    U = np.triu(g.uniform(-1, 1, (d, d)))
+    np.fill_diagonal(U, g.uniform(0.5, 2.0, d))
+    return (P @ U).astype(np.float32), P, perm
+
+
+def test_rotation_of_permuted_triangular_is_the_permutation():
+    Gm, P, _ = _perm_upper(64, 5)
+    R = oracle.rotation(Gm)
+    assert np.abs(R - P).max() < 1e-12
+
+
+# ------------------------------------------------------------------------------------
+# packed format and encode, on inputs whose encoding is known bit by bit
+# ------------------------------------------------------------------------------------
+
+def _half_odd_key(d, seed):
+    """A key of +-0.5 / +-1.5 entries with sum of squares exactly d, so that with an
+    identity rotation z = sqrt(d) x / |x| = x exactly."""
+    g = np.random.default_rng(seed)
+    n1 = 5 * d // 8   # 0.25*n1 + 2.25*(d-n1) = d
+    mag = np.array([0.5] * n1 + [1.5] * (d - n1))
+    g.shuffle(mag)
+    return (mag * g.choice([-1.0, 1.0], d)).astype(np.float32)
+
+
+def _identity_gauss(d, seed=0):
+    g = np.random.default_rng(seed)
+    U = np.triu(g.uniform(-1, 1, (d, d)))
+    np.fill_diagonal(U, g.uniform(0.5, 2.0, d))
+    return U.astype(np.float32)
+
+
+def test_format_bit_positions_and_zero_padding():
+    d = m = 64
+    spec = oracle.Spec(d, m, [(d, 2)])
+    prm = oracle.Params(spec, [_identity_gauss(d)], np.eye(m, d, dtype=np.float32))
+    assert np.abs(prm.rots[0] - np.eye(d)).max() < 1e-14
+    keys = np.zeros((7, d), np.float32)
+    x = _half_odd_key(d, 1)
+    keys[5] = x
+    bits, norms, rnorms = oracle.encode(prm, keys)
+    assert bits.shape == (1, 2 * 2 + 2, 16)
+    c = prm.cent[0, :4]
+    # expected bucket per coordinate: thresholds are -0.98, 0, 0.98
+    idx = np.where(x < -1, 0, np.where(x < 0, 1, np.where(x < 1, 2, 3)))
+    resid = x - c[idx]                 # |x| = 8 = sqrt(d): xhat = c[idx] exactly scaled by 1
+    sgn = (resid >= 0).astype(np.uint32)
+    for j in range(d):
+        for p in range(2):
+            assert (bits[0, p * 2 + j // 32, 5] >> (j % 32)) & 1 == (idx[j] >> p) & 1
+        assert (bits[0, 4 + j // 32, 5] >> (j % 32)) & 1 == sgn[j]
+    assert norms[5, 0] == 8.0
+    assert abs(rnorms[5] - np.linalg.norm(resid)) < 1e-6
+    # zero-vector slots (keys 0..4, 6 and padding 7..15): bucket L/2 = 2, all signs +
+    for i in list(range(5)) + list(range(6, 16)):
+        assert list(bits[0, :, i]) == [0, 0, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF]
+        assert norms[i, 0] == 0.0 and rnorms[i] == 0.0
+
+
+def test_rotation_convention_row_j_gives_coordinate_j():
+    """z_j = <R[j,:], x>: with R = P, coordinate j is x[perm[j]] (a transposed
+    rotation would read x[perm^-1[j]])."""
+    d = 64
+    Gm, P, perm = _perm_upper(d, 7)
+    spec = oracle.Spec(d, 0, [(d, 2)])
+    prm = oracle.Params(spec, [Gm], None)
+    x = _half_odd_key(d, 3)
+    bits, _, _ = oracle.encode(prm, x[None])
+    codes, _ = oracle.unpack(spec, bits, 1)
+    z = x[perm]
+    want = np.where(z < -1, 0, np.where(z < 0, 1, np.where(z < 1, 2, 3)))
+    np.testing.assert_array_equal(codes[0], want)
+
+
+def test_two_groups_follow_the_channel_list():
+    d = 64
+    chan = np.random.default_rng(2).permutation(d).astype(np.int32)
+    spec = oracle.Spec(d, 0, [(32, 2), (32, 1)], chan)
+    prm = oracle.Params(spec, [_identity_gauss(32, 1), _identity_gauss(32, 2)], None)
+    x = np.zeros(d, np.float32)
+    x[chan[:32]] = _half_odd_key(32, 4)
+    x[chan[32:]] = _half_odd_key(32, 5)
+    bits, norms, _ = oracle.encode(prm, x[None])
+    codes, _ = oracle.unpack(spec, bits, 1)
+    z0, z1 = x[chan[:32]], x[chan[32:]]
+    np.testing.assert_array_equal(codes[0, :32], np.where(z0 < -1, 0, np.where(z0 < 0, 1, np.where(z0 < 1, 2, 3))))
+    np.testing.assert_array_equal(codes[0, 32:], (z1 >= 0).astype(int))
+    np.testing.assert_allclose(norms[0], [math.sqrt(32)] * 2, rtol=1e-7)
+
+
+# ------------------------------------------------------------------------------------
+# consistency of the stages with the decoder (random small shapes)
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_residual_signs_and_norms_are_those_of_the_decoder(seed):
+    g = np.random.default_rng(100 + seed)
+    d = int(g.choice([32, 64, 96, 128]))
+    m = int(g.choice([32, 128]))
+    b = int(g.integers(1, 4))
+    spec = oracle.Spec(d, m, [(d, b)])
+    S = g.standard_normal((m, d)).astype(np.float32)
+    prm = oracle.Params(spec, [g.standard_normal((d, d)).astype(np.float32)], S)
+    x = (g.standard_normal((40, d)) * g.uniform(0.1, 5, (40, 1))).astype(np.float32)
+    bits, norms, rnorms = oracle.encode(prm, x)
+    xhat = oracle.decode(prm, bits, norms, 40)
+    r = x.astype(np.float64) - xhat
+    np.testing.assert_allclose(rnorms[:40], np.linalg.norm(r, axis=1), rtol=1e-6)
+    np.testing.assert_allclose(norms[:40, 0], np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-7)
+    _, signs = oracle.unpack(spec, bits, 40)
+    p = r @ S.astype(np.float64).T
+    clear = np.abs(p) > 1e-9 * np.abs(p).max()
+    np.testing.assert_array_equal(signs[clear], (p[clear] >= 0).astype(np.uint8))
+    # MSE-only scores are exactly <q, decode(x)>
+    spec0 = oracle.Spec(d, 0, [(d, b)])
+    prm0 = oracle.Params(spec0, [g.standard_normal((d, d)).astype(np.float32)], None)
+    b0, n0, r0 = oracle.encode(prm0, x)
+    q = g.standard_normal((3, d)).astype(np.float32)
+    s0 = oracle.score(prm0, b0, n0, r0, 40, q)
+    ref = q.astype(np.float64) @ oracle.decode(prm0, b0, n0, 40).T
+    np.testing.assert_allclose(s0, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_zero_key_contributes_nothing():
+    spec = oracle.Spec(128, 128, [(128, 3)])
+    g = np.random.default_rng(9)
+    prm = oracle.Params(spec, [g.standard_normal((128, 128)).astype(np.float32)],
+                        g.standard_normal((128, 128)).astype(np.float32))
+    bits, norms, rnorms = oracle.encode(prm, np.zeros((1, 128), np.float32))
+    codes, signs = oracle.unpack(spec, bits, 1)
+    assert (codes == 4).all() and (signs == 1).all() and norms[0, 0] == 0 and rnorms[0] == 0
+    assert oracle.score(prm, bits, norms, rnorms, 1, g.standard_normal((2, 128)).astype(np.float32)).tolist() == [[0.0], [0.0]]
+
+
+# ------------------------------------------------------------------------------------
+# distortion (turboquant-pytorch write-up, performance section: 0.034 measured, 0.043 bound)
+# ------------------------------------------------------------------------------------
+
+def _sphere_marginal_mse(bits, d):
+    """E[(z - Q(z))^2] for z = sqrt(d) u_1, u uniform on the unit sphere in R^d
+    (u_1 has density proportional to (1-t^2)^((d-3)/2)), by quadrature."""
+    c, t, _, _ = oracle.codebook(bits)
+    logB = math.lgamma(0.5) + math.lgamma((d - 1) / 2) - math.lgamma(d / 2)
+    f = lambda s: math.exp(((d - 3) / 2) * math.log1p(-s * s / d) - logB) / math.sqrt(d)  # density of z
+    edges = np.concatenate([[-math.sqrt(d)], t, [math.sqrt(d)]])
+    tot = 0.0
+    for k in range(len(c)):
+        tot += integrate.quad(lambda s: (s - c[k]) ** 2 * f(s), edges[k], edges[k + 1], epsabs=1e-13, epsrel=1e-11)[0]
+    return tot
+
+
+def _unit_gaussian_distortion(bits, d, n, seed):
+    g = np.random.default_rng(seed)
+    spec = oracle.Spec(d, 0, [(d, bits)])
+    prm = oracle.Params(spec, [g.standard_normal((d, d)).astype(np.float32)], None)
+    x = g.standard_normal((n, d))
+    x = (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+    bits_, norms, _ = oracle.encode(prm, x)
+    err = ((x.astype(np.float64) - oracle.decode(prm, bits_, norms, n)) ** 2).sum(axis=1)
+    return err.mean(), err.std() / math.sqrt(n)
+
+
+def test_three_bit_distortion_matches_the_reported_value():
+    gold = dict(l.split() for l in open(os.path.join(GOLDEN, "p3_mse_distortion.txt")) if not l.startswith("#"))
+    d, b = int(gold["d"]), int(gold["bits"])
+    mean, se = _unit_gaussian_distortion(b, d, 6000, 11)
+    assert round(mean, 3) == float(gold["measured"])
+    assert mean < float(gold["bound"])
+    assert abs(mean - _sphere_marginal_mse(b, d)) < 4 * se + 1e-5
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_distortion_equals_sphere_marginal_expectation(bits):
+    mean, se = _unit_gaussian_distortion(bits, 128, 4000, 20 + bits)
+    assert abs(mean - _sphere_marginal_mse(bits, 128)) < 4 * se + 1e-5
+    assert mean < math.sqrt(3) * math.pi / 2 * 4.0 ** (-bits)
+
+
+# ------------------------------------------------------------------------------------
+# the estimator: unbiased, with the sign sketch's closed-form variance; MSE-only is biased
+# ------------------------------------------------------------------------------------
+
+def _est_over_S(x, q, rot_gauss, bits, nseeds, seed0):
+    d = x.shape[0]
+    spec = oracle.Spec(d, d, [(d, bits)])
+    prm = oracle.Params(spec, [rot_gauss], np.zeros((d, d), np.float32))
+    out = np.empty(nseeds)
+    for s in range(nseeds):
+        prm.proj = np.random.default_rng(seed0 + s).standard_normal((d, d)).astype(np.float32)
+        b_, n_, r_ = oracle.encode(prm, x[None])
+        out[s] = oracle.score(prm, b_, n_, r_, 1, q[None])[0, 0]
+    return out, prm
+
+
+@pytest.mark.slow
+def test_estimator_unbiased_with_closed_form_variance_over_projections():
+    g = np.random.default_rng(31)
+    d = 128
+    x = (g.standard_normal(d) * 2).astype(np.float32)
+    G = g.standard_normal((d, d)).astype(np.float32)
+    # a query with a large component along the residual so that a wrong sketch
+    # scale or sign would show as a bias
+    spec0 = oracle.Spec(d, 0, [(d, 2)])
+    prm0 = oracle.Params(spec0, [G], None)
+    b0, n0, _ = oracle.encode(prm0, x[None])
+    r = x - oracle.decode(prm0, b0, n0, 1)[0]
+    rho = np.linalg.norm(r)
+    q = (3 * r / rho + g.standard_normal(d)).astype(np.float32)
+    est, prm = _est_over_S(x, q, G, 2, 3000, 5000)
+    truth = float(q.astype(np.float64) @ x.astype(np.float64))
+    se = est.std(ddof=1) / math.sqrt(len(est))
+    assert abs(est.mean() - truth) < 4 * se
+    qd = q.astype(np.float64)
+    var = ((math.pi / 2) * rho ** 2 * (qd @ qd) - (qd @ r) ** 2) / d
+    rel = est.var(ddof=1) / var
+    assert abs(rel - 1) < 4 * math.sqrt(2 / (len(est) - 1))
+
+
+@pytest.mark.slow
+def test_estimator_unbiased_over_rotations_and_projections():
+    g = np.random.default_rng(41)
+    d = 64
+    x = g.standard_normal(d).astype(np.float32)
+    q = (x + g.standard_normal(d)).astype(np.float32)
+    spec = oracle.Spec(d, d, [(d, 1)])
+    vals = []
+    for s in range(1500):
+        h = np.random.default_rng(9000 + s)
+        prm = oracle.Params(spec, [h.standard_normal((d, d)).astype(np.float32)],
+                            h.standard_normal((d, d)).astype(np.float32))
+        b_, n_, r_ = oracle.encode(prm, x[None])
+        vals.append(oracle.score(prm, b_, n_, r_, 1, q[None])[0, 0])
+    vals = np.array(vals)
+    truth = float(q.astype(np.float64) @ x.astype(np.float64))
+    assert abs(vals.mean() - truth) < 4 * vals.std(ddof=1) / math.sqrt(len(vals))
+
+
+@pytest.mark.slow
+def test_mse_only_one_bit_shrinks_inner_products_by_two_over_pi():
+    """The bias the sign sketch removes (tambur.pub article: an MSE-optimal quantiser
+    gives a biased inner-product estimate)."""
+    g = np.random.default_rng(51)
+    d = 128
+    spec = oracle.Spec(d, 0, [(d, 1)])
+    ratios = []
+    for s in range(300):
+        h = np.random.default_rng(7000 + s)
+        prm = oracle.Params(spec, [h.standard_normal((d, d)).astype(np.float32)], None)
+        x = h.standard_normal((8, d)).astype(np.float32)
+        b_, n_, r_ = oracle.encode(prm, x)
+        xhat = oracle.decode(prm, b_, n_, 8)
+        ratios += list((x.astype(np.float64) * xhat).sum(1) / (x.astype(np.float64) ** 2).sum(1))
+    assert abs(np.mean(ratios) - 2 / math.pi) < 0.01
+
+
+# ------------------------------------------------------------------------------------
+# top-k
+# ------------------------------------------------------------------------------------
+
+def test_topk_orders_by_score_then_lower_index():
+    g = np.random.default_rng(3)
+    s = np.round(g.standard_normal((5, 400)), 1)     # many exact ties
+    vals, idx = oracle.topk(s, 17)
+    for q in range(5):
+        order = np.lexsort((np.arange(400), -s[q]))[:17]
+        np.testing.assert_array_equal(idx[q], order)
+        np.testing.assert_array_equal(vals[q], s[q, order])
+
+
+def test_workload_generators_are_method_free_and_seeded():
+    cfg = workloads.CONFIGS["decode3b"]
+    a = workloads.keys(cfg, n=64)
+    b = workloads.keys(cfg, n=64)
+    np.testing.assert_array_equal(a, b)
+    assert a.shape == (2, 64, 128)
+    # bf16-representable values
+    back = (workloads.bf16_bits(a).astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(back, a)
