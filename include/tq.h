@@ -1,0 +1,172 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant packed-key library.
+ *
+ * The method (turboquant-pytorch write-up on discuss.pytorch.kr, section on the
+ * two-stage algorithm; tambur.pub article on TurboQuant; tistory series part 11,
+ * section 3 on format-aware kernels):
+ *   stage 1: rotate each key with a random orthogonal matrix and quantise every
+ *            rotated coordinate on its own against a Lloyd-Max codebook that is
+ *            precomputed for the normal distribution the rotation produces;
+ *   stage 2: project the stage-1 residual with a Gaussian matrix S and keep one
+ *            sign bit per projection row (QJL), plus the residual's norm;
+ *   scoring: unbiased inner-product estimates of full-precision queries against
+ *            the packed keys (attention logits, vector-search scores), optionally
+ *            reduced to a per-query top-k.
+ *
+ * Conventions for every entry point:
+ *   - All pointers marked (device) are device memory owned by the caller; the
+ *     library never allocates, frees or retains them. (host) pointers are host
+ *     memory read or written before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Device work is
+ *     enqueued asynchronously on it; argument checks run first and return a
+ *     negative status with nothing enqueued.
+ *   - Returns TQ_OK (0) or a negative tq_status. TQ_ERR_DEVICE reports a failed
+ *     launch (the HIP error is not cleared). tq_status_string() names a code.
+ *   - Results are bit-identical from run to run for identical inputs.
+ *   - Calls are thread-safe; the library holds no mutable global state.
+ *   - Non-finite inputs give unspecified (but memory-safe) results.
+ *
+ * Packed bank format (one "bank" = the keys of one (layer, batch, kv-head), or a
+ * whole search database). With W = sum_g b_g*d_g/32 + m/32 words per key and
+ * n_pad = 16*ceil(n/16):
+ *   bits   (uint32) [banks][n_pad/16][W][16]: element [b][t][w][i] is word w of key
+ *          16*t+i. Word order inside a key: for each channel group g, for each
+ *          codebook bit-plane p < b_g, d_g/32 words (word k, bit t = bit p of the
+ *          bucket index of rotated coordinate 32k+t of group g); then m/32 sign
+ *          words (word k, bit t = [row 32k+t of S times the residual >= 0]).
+ *   norms  (float)  [banks][n_pad][n_groups]: |x_g| per group.
+ *   rnorms (float)  [banks][n_pad]: |residual|.
+ *   Slots n..n_pad-1 hold the encoding of the zero vector.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_ERR_ARG = -1,         /* null pointer, bad size, inconsistent parameters */
+    TQ_ERR_UNSUPPORTED = -2, /* a valid request this build has no kernel for */
+    TQ_ERR_DEVICE = -3,      /* a HIP launch failed */
+    TQ_ERR_WORKSPACE = -4    /* workspace missing or smaller than tq_workspace_bytes() */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef enum { TQ_OP_ENCODE = 0, TQ_OP_SCORE = 1, TQ_OP_TOPK = 2 } tq_op;
+
+/* Parameters of one encoding. Dimensions and the codebooks are host values;
+ * the matrices are (device) pointers read by the kernels.
+ *   d            key dimension; d = group_dim[0] (+ group_dim[1])
+ *   m            sign-sketch rows (QJL); a multiple of 32, >= 32
+ *   n_groups     1, or 2 for a split of the channels into two groups that are
+ *                rotated and quantised separately (mixed bit widths)
+ *   group_dim    channels per group, multiples of 32
+ *   group_bits   codebook bits per group, 1..3 (the total budget per channel is
+ *                group_bits + the shared 1-bit sketch)
+ *   centroids    per group, 2^bits Lloyd-Max centroids in ascending order, in
+ *                unit-variance units (tq_make_codebook); must be symmetric,
+ *                c[L-1-i] == -c[i]
+ *   thresholds   per group, the 2^bits - 1 decision thresholds (midpoints)
+ *   group_chan   (device) int32[d]: group 0's channels ascending, then group 1's;
+ *                NULL = identity (required NULL when n_groups == 1)
+ *   rot          (device) float32: group 0's d_0 x d_0 rotation row-major, then
+ *                group 1's; rotated coordinate j of group g = row j . x_g
+ *   proj         (device) float32 [m][d] row-major: S, columns in channel order */
+typedef struct {
+    int32_t d, m, n_groups;
+    int32_t group_dim[2];
+    int32_t group_bits[2];
+    float centroids[2][16];
+    float thresholds[2][15];
+    const int32_t *group_chan;
+    const float *rot;
+    const float *proj;
+} tq_params;
+
+/* (device) arrays of one or more banks, laid out as described above. */
+typedef struct {
+    uint32_t *bits;
+    float *norms;
+    float *rnorms;
+} tq_bank;
+
+/* Lloyd-Max codebook for N(0,1) with 2^bits levels, 1 <= bits <= 4, computed on
+ * the host in fp64 and rounded to float (turboquant-pytorch write-up, stage 1:
+ * the codebook is precomputed for the normal distribution of the rotated
+ * coordinates). centroids[2^bits], thresholds[2^bits - 1] (host); mse_out
+ * (host, nullable) receives the fp64 mean squared error. Deterministic. */
+int tq_make_codebook(int bits, float *centroids, float *thresholds, double *mse_out);
+
+/* Random orthogonal rotation (same write-up, stage 1): the Q factor of a QR
+ * decomposition of the d x d matrix `gauss` (host, row-major, expected i.i.d.
+ * N(0,1)), with column signs fixed so that the triangular factor has a positive
+ * diagonal. Host fp64 computation; rot (host) receives d x d floats row-major.
+ * TQ_ERR_ARG if gauss is rank-deficient. */
+int tq_make_rotation(int d, const float *gauss, float *rot);
+
+/* Bank geometry for n keys: 32-bit words per key, n_pad, and bytes per key of the
+ * three arrays together (words*4 + 4*n_groups + 4). Host only. */
+int tq_bank_layout(const tq_params *p, int64_t n, int64_t *words_per_key, int64_t *n_pad, int64_t *bytes_per_key);
+
+/* Device workspace bytes needed by `op` (a tq_op) for these sizes; 0 on bad
+ * arguments. Pass at least this much, 256-byte aligned, to the call. */
+size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k);
+
+/* Encode (stages 1 and 2) keys (device) [banks][n][d] of dtype TQ_F32 or TQ_BF16
+ * into `out` (device arrays sized by tq_bank_layout for `banks` banks). Uses
+ * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, ...). */
+int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t n, const tq_bank *out,
+              void *workspace, size_t ws_bytes, void *stream);
+
+/* Query preparation (per query: R_g q_g and S q, once, as the estimator's
+ * operands; same write-up, usage example: the query stays at full precision).
+ * q (device) float32 [banks][G][d]. Writes the prepared operands into
+ * `workspace` (device), of tq_workspace_bytes(TQ_OP_SCORE, ...) bytes, for
+ * tq_score_prepared / tq_topk_prepared. */
+int tq_prepare_queries(const tq_params *p, const float *q, int64_t banks, int32_t G, void *workspace,
+                       size_t ws_bytes, void *stream);
+
+/* Estimated inner products of prepared queries against packed banks:
+ *   est = sum_g (nu_g / sqrt(d_g)) <R_g q_g, c_g[idx_g]>
+ *       + sqrt(pi/2) / m * rho * <S q, 2*signs - 1>
+ * (turboquant-pytorch write-up: stage 2 makes this estimate unbiased; usage
+ * example: inner_product(query, compressed)). scores (device) float32
+ * [banks][G][n]; query row g of bank b uses bank b (GQA: the caller arranges the
+ * G query heads sharing a kv head as one bank's queries). */
+int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
+                      const void *workspace, float *scores, void *stream);
+
+/* tq_prepare_queries followed by tq_score_prepared. */
+int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
+             float *scores, void *workspace, size_t ws_bytes, void *stream);
+
+/* Per query, the k largest estimates (vector search over the packed database;
+ * tambur.pub article, vector-search paragraph), largest first, equal estimates
+ * by lower key index. vals (device) float32 [banks][G][k], idx (device) int32
+ * [banks][G][k]. 1 <= k <= 64 and k <= n. The score rows are never written to
+ * memory. Workspace: tq_workspace_bytes(TQ_OP_TOPK, ...). */
+int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G, int32_t k,
+            float *vals, int32_t *idx, void *workspace, size_t ws_bytes, void *stream);
+
+/* Measurement kernels (not part of the method):
+ * fp32 logits against unquantized keys, scores[b][g][i] = q[b][g] . keys[b][i]
+ * (keys, q, scores device float32; the comparison the tambur.pub article makes
+ * between 4-bit keys and 32-bit keys), and a plain device-to-device copy used to
+ * calibrate the achievable HBM bandwidth and the traffic counters. */
+int tq_fp32_logits(const float *keys, int64_t banks, int64_t n, int32_t d, const float *q, int32_t G, float *scores,
+                   void *stream);
+int tq_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+const char *tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,417 @@
+// C-ABI host library of the gfx950 TurboQuant packed-key path: argument checks, host
+// parameter construction (codebook, rotation), workspace planning and kernel dispatch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_encode.h"
+#include "tq_score.h"
+#include "tq_measure.h"
+
+using namespace tq;
+
+// ----------------------------------------------------------------------------------------
+// Lloyd-Max codebook for N(0,1), computed on the positive half-line (the density is
+// symmetric, so the optimum is): positive centroids c_1 < ... < c_{L/2}, thresholds
+// 0 = t_0 < t_1 < ... ; iterate t_k = (c_k + c_{k+1})/2 and c_k = E[X | t_{k-1} <= X < t_k].
+// Tail masses use erfc so that outer cells keep full relative precision.
+// (turboquant-pytorch write-up, stage 1: a Lloyd-Max codebook precomputed for the normal
+// distribution of the rotated coordinates.)
+// ----------------------------------------------------------------------------------------
+static double upper_mass(double x) { return 0.5 * erfc(x / sqrt(2.0)); }  // P(X >= x)
+static double density(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); }
+
+extern "C" int tq_make_codebook(int bits, float *centroids, float *thresholds, double *mse_out) {
+    if (bits < 1 || bits > 4 || !centroids || (bits > 0 && !thresholds)) return TQ_ERR_ARG;
+    const int L = 1 << bits, H = L / 2;
+    double c[8], t[9];
+    for (int k = 0; k < H; ++k) c[k] = 3.0 * (k + 0.5) / H;  // start: even grid on (0, 3)
+    t[0] = 0.0;
+    for (int iter = 0; iter < 1000000; ++iter) {
+        for (int k = 1; k < H; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+        t[H] = INFINITY;
+        double change = 0.0;
+        for (int k = 0; k < H; ++k) {
+            const double a = t[k], b = t[k + 1];
+            const double mass = upper_mass(a) - (isinf(b) ? 0.0 : upper_mass(b));
+            const double first = density(a) - (isinf(b) ? 0.0 : density(b));
+            const double nc = first / mass;
+            change = fmax(change, fabs(nc - c[k]));
+            c[k] = nc;
+        }
+        if (change < 1e-16) break;
+    }
+    for (int k = 1; k < H; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    t[H] = INFINITY;
+    // MSE over both halves: 2 * sum_k E[(X - c_k)^2 ; cell k]
+    double mse = 0.0;
+    for (int k = 0; k < H; ++k) {
+        const double a = t[k], b = t[k + 1];
+        const double m0 = upper_mass(a) - (isinf(b) ? 0.0 : upper_mass(b));
+        const double m1 = density(a) - (isinf(b) ? 0.0 : density(b));
+        const double m2 = m0 + a * density(a) - (isinf(b) ? 0.0 : b * density(b));
+        mse += 2.0 * (m2 - 2.0 * c[k] * m1 + c[k] * c[k] * m0);
+    }
+    for (int k = 0; k < H; ++k) {
+        centroids[H + k] = (float)c[k];
+        centroids[H - 1 - k] = -(float)c[k];
+    }
+    for (int k = 0; k < H; ++k) {
+        const float tk = (float)t[k];
+        thresholds[H - 1 + k] = tk;
+        if (k > 0) thresholds[H - 1 - k] = -tk;
+    }
+    if (mse_out) *mse_out = mse;
+    return TQ_OK;
+}
+
+// ----------------------------------------------------------------------------------------
+// Random orthogonal rotation: modified Gram-Schmidt (applied twice per column) on the
+// columns of the Gaussian matrix. The resulting triangular factor has a positive
+// diagonal by construction, which fixes the column signs: this is the unique
+// sign-fixed Q factor of `gauss` (turboquant-pytorch write-up, stage 1).
+// ----------------------------------------------------------------------------------------
+extern "C" int tq_make_rotation(int d, const float *gauss, float *rot) {
+    if (d <= 0 || d > 4096 || !gauss || !rot) return TQ_ERR_ARG;
+    std::vector<double> Q((size_t)d * d);  // column-major: column j at Q[j*d]
+    for (int j = 0; j < d; ++j) {
+        double *v = &Q[(size_t)j * d];
+        for (int i = 0; i < d; ++i) v[i] = gauss[(size_t)i * d + j];
+        const double n0 = sqrt([&] { double s = 0; for (int i = 0; i < d; ++i) s += v[i] * v[i]; return s; }());
+        for (int pass = 0; pass < 2; ++pass)
+            for (int k = 0; k < j; ++k) {
+                const double *u = &Q[(size_t)k * d];
+                double r = 0.0;
+                for (int i = 0; i < d; ++i) r += u[i] * v[i];
+                for (int i = 0; i < d; ++i) v[i] -= r * u[i];
+            }
+        double nv = 0.0;
+        for (int i = 0; i < d; ++i) nv += v[i] * v[i];
+        nv = sqrt(nv);
+        if (!(nv > 1e-10 * (n0 > 0 ? n0 : 1.0))) return TQ_ERR_ARG;  // rank-deficient
+        for (int i = 0; i < d; ++i) v[i] /= nv;
+    }
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) rot[(size_t)i * d + j] = (float)Q[(size_t)j * d + i];
+    return TQ_OK;
+}
+
+// ----------------------------------------------------------------------------------------
+// argument checks and geometry
+// ----------------------------------------------------------------------------------------
+static int check_params(const tq_params *p) {
+    if (!p) return TQ_ERR_ARG;
+    if (p->n_groups < 1 || p->n_groups > 2) return TQ_ERR_ARG;
+    int sum = 0;
+    for (int g = 0; g < p->n_groups; ++g) {
+        if (p->group_dim[g] <= 0 || p->group_dim[g] % 32) return TQ_ERR_ARG;
+        if (p->group_bits[g] < 1 || p->group_bits[g] > 3) return TQ_ERR_ARG;
+        sum += p->group_dim[g];
+        const int L = 1 << p->group_bits[g];
+        for (int i = 0; i < L; ++i) {
+            if (!isfinite(p->centroids[g][i])) return TQ_ERR_ARG;
+            if (p->centroids[g][L - 1 - i] != -p->centroids[g][i]) return TQ_ERR_UNSUPPORTED;  // symmetric only
+            if (i + 1 < L && !(p->centroids[g][i] < p->centroids[g][i + 1])) return TQ_ERR_ARG;
+        }
+        for (int i = 0; i + 1 < L; ++i)
+            if (!(p->centroids[g][i] <= p->thresholds[g][i] && p->thresholds[g][i] <= p->centroids[g][i + 1]))
+                return TQ_ERR_ARG;
+    }
+    if (sum != p->d || p->d > 1024) return TQ_ERR_ARG;
+    if (p->m < 32 || p->m > 1024 || p->m % 32) return TQ_ERR_ARG;
+    if (!p->rot || !p->proj) return TQ_ERR_ARG;
+    return TQ_OK;
+}
+
+static int words_per_key(const tq_params *p) {
+    int w = p->m / 32;
+    for (int g = 0; g < p->n_groups; ++g) w += p->group_bits[g] * p->group_dim[g] / 32;
+    return w;
+}
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+extern "C" int tq_bank_layout(const tq_params *p, int64_t n, int64_t *wpk, int64_t *n_pad, int64_t *bpk) {
+    const int rc = check_params(p);
+    if (rc) return rc;
+    if (n < 0) return TQ_ERR_ARG;
+    const int W = words_per_key(p);
+    if (wpk) *wpk = W;
+    if (n_pad) *n_pad = 16 * ((n + 15) / 16);
+    if (bpk) *bpk = 4 * (int64_t)W + 4 * (int64_t)p->n_groups + 4;
+    return TQ_OK;
+}
+
+// ----------------------------------------------------------------------------------------
+// layout dispatch: the scorer is compiled for these (groups, dims, bits, m)
+// ----------------------------------------------------------------------------------------
+#define TQ_LAYOUTS(X)            \
+    X(1, 128, 1, 0, 0, 128)      \
+    X(1, 128, 2, 0, 0, 128)      \
+    X(1, 128, 3, 0, 0, 128)      \
+    X(1, 64, 1, 0, 0, 64)        \
+    X(1, 64, 2, 0, 0, 64)        \
+    X(1, 256, 1, 0, 0, 256)      \
+    X(1, 256, 2, 0, 0, 256)      \
+    X(1, 256, 3, 0, 0, 256)      \
+    X(1, 768, 1, 0, 0, 768)      \
+    X(1, 768, 2, 0, 0, 768)      \
+    X(1, 768, 3, 0, 0, 768)      \
+    X(2, 32, 2, 96, 1, 128)
+
+static bool layout_is(const tq_params *p, int ng, int d0, int b0, int d1, int b1, int m) {
+    if (p->n_groups != ng || p->m != m || p->group_dim[0] != d0 || p->group_bits[0] != b0) return false;
+    if (ng > 1 && (p->group_dim[1] != d1 || p->group_bits[1] != b1)) return false;
+    return true;
+}
+
+// Calls f(Layout{}) for the matching layout; returns TQ_ERR_UNSUPPORTED if none.
+template <class F>
+static int with_layout(const tq_params *p, F &&f) {
+#define TQ_TRY(ng, d0, b0, d1, b1, m) \
+    if (layout_is(p, ng, d0, b0, d1, b1, m)) return f(Layout<ng, d0, b0, d1, b1, m>{});
+    TQ_LAYOUTS(TQ_TRY)
+#undef TQ_TRY
+    return TQ_ERR_UNSUPPORTED;
+}
+
+// query-operand workspace: frags [banks][Gpad/4][NF][64][16 B], consts [banks][Gpad][NCLS][2] f64
+struct PrepPlan {
+    int Gpad, NF, NCLS;
+    size_t frag_bytes, const_off, total;
+};
+static PrepPlan prep_plan(int NF, int NCLS, int64_t banks, int32_t G) {
+    PrepPlan pl;
+    pl.Gpad = 4 * ((G + 3) / 4);
+    pl.NF = NF;
+    pl.NCLS = NCLS;
+    pl.frag_bytes = (size_t)banks * (pl.Gpad / 4) * NF * 1024;
+    pl.const_off = align256(pl.frag_bytes);
+    pl.total = pl.const_off + align256((size_t)banks * pl.Gpad * NCLS * 16);
+    return pl;
+}
+
+static size_t encode_ws(const tq_params *p) { return align256((size_t)p->m * p->d * 4); }
+
+extern "C" size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k) {
+    if (check_params(p) || banks < 0 || n < 0) return 0;
+    if (op == TQ_OP_ENCODE) return encode_ws(p);
+    if (G < 1) return 0;
+    size_t out = 0;
+    const int rc = with_layout(p, [&](auto l) {
+        using L = decltype(l);
+        out = prep_plan(L::NF, L::NCLS, banks, G).total;
+        return TQ_OK;
+    });
+    if (rc) return 0;
+    if (op == TQ_OP_SCORE) return out;
+    if (op == TQ_OP_TOPK) {
+        if (k < 1 || k > 64) return 0;
+        return out + align256(topk_partial_bytes(banks, G, n, k));
+    }
+    return 0;
+}
+
+static int launch_status() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE; }
+
+static EncArgs enc_args(const tq_params *p) {
+    EncArgs a;
+    memset(&a, 0, sizeof(a));
+    a.d = p->d;
+    a.m = p->m;
+    a.ng = p->n_groups;
+    int off = 0, word = 0;
+    for (int g = 0; g < p->n_groups; ++g) {
+        a.gdim[g] = p->group_dim[g];
+        a.gbits[g] = p->group_bits[g];
+        a.goff[g] = off;
+        a.gword[g] = word;
+        off += p->group_dim[g];
+        word += p->group_bits[g] * p->group_dim[g] / 32;
+        for (int i = 0; i < 16; ++i) a.cent[g][i] = p->centroids[g][i];
+        for (int i = 0; i < 15; ++i) a.thr[g][i] = p->thresholds[g][i];
+        a.sqrt_d[g] = sqrt((double)p->group_dim[g]);
+    }
+    a.sword = word;
+    a.W = word + p->m / 32;
+    return a;
+}
+
+extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t n, const tq_bank *out,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
+    if (banks == 0 || n == 0) return TQ_OK;
+    if (!keys || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
+    if (!workspace || ws_bytes < encode_ws(p) || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    const int64_t n_tiles = (n + 15) / 16;
+    if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    const EncArgs a = enc_args(p);
+    float *sp = (float *)workspace;
+    const long tot = (long)p->m * p->d;
+    hipLaunchKernelGGL(enc_prep_proj_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p->proj, p->rot,
+                       p->group_chan, a, sp);
+    if ((rc = launch_status())) return rc;
+    const size_t smem = enc_smem_bytes(p->d, p->m);
+    const dim3 grid((unsigned)(banks * n_tiles));
+    if (dtype == TQ_F32) {
+        (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)n, (int)n_tiles,
+                           p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms);
+    } else {
+        (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)n,
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms);
+    }
+    return launch_status();
+}
+
+static PrepArgs prep_args(const tq_params *p) {
+    PrepArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    for (int g = 0; g < p->n_groups; ++g) {
+        const int b = p->group_bits[g], L = 1 << b;
+        double total = 0.0;
+        for (int s = 0; s < walsh_planes(b); ++s) {
+            const int mask = walsh_mask(b, s);
+            double acc = 0.0;
+            for (int idx = 0; idx < L; ++idx) {
+                double chi = 1.0;
+                for (int bit = 0; bit < b; ++bit)
+                    if (mask & (1 << bit)) chi *= ((idx >> bit) & 1) ? 1.0 : -1.0;
+                acc += (double)p->centroids[g][idx] * chi;
+            }
+            const double chat = acc / L;
+            pa.walsh[g][s] = 2.0 * chat;
+            total += chat;
+        }
+        pa.cmax[g] = total;
+    }
+    return pa;
+}
+
+extern "C" int tq_prepare_queries(const tq_params *p, const float *q, int64_t banks, int32_t G, void *workspace,
+                                  size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || G < 1) return TQ_ERR_ARG;
+    if (banks == 0) return TQ_OK;
+    if (!q) return TQ_ERR_ARG;
+    return with_layout(p, [&](auto l) {
+        using L = decltype(l);
+        const PrepPlan pl = prep_plan(L::NF, L::NCLS, banks, G);
+        if (!workspace || ws_bytes < pl.total || ((uintptr_t)workspace & 255)) return (int)TQ_ERR_WORKSPACE;
+        if (banks * pl.Gpad > INT32_MAX) return (int)TQ_ERR_UNSUPPORTED;
+        int8_t *frags = (int8_t *)workspace;
+        double *consts = (double *)((char *)workspace + pl.const_off);
+        hipLaunchKernelGGL(qprep_kernel<L>, dim3((unsigned)(banks * pl.Gpad)), dim3(256), 0, (hipStream_t)stream, q,
+                           p->rot, p->proj, p->group_chan, prep_args(p), (int)G, pl.Gpad, frags, consts);
+        return launch_status();
+    });
+}
+
+static ScoreScale score_scale(const tq_params *p) {
+    ScoreScale s;
+    s.inv_sqrt_d[0] = 1.0 / sqrt((double)p->group_dim[0]);
+    s.inv_sqrt_d[1] = p->n_groups > 1 ? 1.0 / sqrt((double)p->group_dim[1]) : 0.0;
+    s.qjl = sqrt(M_PI / 2.0) / (double)p->m;
+    return s;
+}
+
+template <class L, int RT>
+static int launch_score(const tq_bank *in, int64_t banks, int64_t n, int32_t G, const PrepPlan &pl, const void *ws,
+                        float *scores, const ScoreScale &sc, hipStream_t st) {
+    const int64_t n_tiles = (n + 15) / 16;
+    const int64_t target_waves = 256 * 16;
+    int64_t tpw = (banks * n_tiles + target_waves - 1) / target_waves;
+    if (tpw < 1) tpw = 1;
+    const int64_t wpb = (n_tiles + tpw - 1) / tpw;
+    const int64_t waves = banks * wpb;
+    if ((waves + 3) / 4 > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+    const int8_t *frags = (const int8_t *)ws;
+    const double *consts = (const double *)((const char *)ws + pl.const_off);
+    hipLaunchKernelGGL((score_kernel<L, RT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, in->bits, in->norms,
+                       in->rnorms, frags, consts, scores, (int)banks, (long)n, (int)n_tiles, (int)G, pl.Gpad, (int)tpw,
+                       (int)wpb, sc);
+    return launch_status();
+}
+
+extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
+                                 const void *workspace, float *scores, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
+    if (banks == 0 || n == 0) return TQ_OK;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !scores) return TQ_ERR_ARG;
+    if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    if (G > 16) return TQ_ERR_UNSUPPORTED;
+    const ScoreScale sc = score_scale(p);
+    return with_layout(p, [&](auto l) {
+        using L = decltype(l);
+        const PrepPlan pl = prep_plan(L::NF, L::NCLS, banks, G);
+        hipStream_t st = (hipStream_t)stream;
+        switch (pl.Gpad / 4) {
+            case 1: return launch_score<L, 1>(in, banks, n, G, pl, workspace, scores, sc, st);
+            case 2: return launch_score<L, 2>(in, banks, n, G, pl, workspace, scores, sc, st);
+            case 3: return launch_score<L, 3>(in, banks, n, G, pl, workspace, scores, sc, st);
+            default: return launch_score<L, 4>(in, banks, n, G, pl, workspace, scores, sc, st);
+        }
+    });
+}
+
+extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
+                        float *scores, void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
+    if (banks == 0 || n == 0) return TQ_OK;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q) return TQ_ERR_ARG;
+    if (G > 16) return TQ_ERR_UNSUPPORTED;
+    if ((rc = tq_prepare_queries(p, q, banks, G, workspace, ws_bytes, stream))) return rc;
+    return tq_score_prepared(p, in, banks, n, G, workspace, scores, stream);
+}
+
+extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
+                       int32_t k, float *vals, int32_t *idx, void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || n < 0 || G < 1 || k < 1 || k > 64 || k > n) return TQ_ERR_ARG;
+    if (banks == 0) return TQ_OK;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx) return TQ_ERR_ARG;
+    (void)workspace;
+    (void)ws_bytes;
+    (void)stream;
+    return TQ_ERR_UNSUPPORTED;
+}
+
+extern "C" int tq_fp32_logits(const float *keys, int64_t banks, int64_t n, int32_t d, const float *q, int32_t G,
+                              float *scores, void *stream) {
+    if (banks < 0 || n < 0 || d <= 0 || d % 4 || G < 1) return TQ_ERR_ARG;
+    if (banks == 0 || n == 0) return TQ_OK;
+    if (!keys || !q || !scores) return TQ_ERR_ARG;
+    if (d > 256 || G > 32) return TQ_ERR_UNSUPPORTED;
+    return launch_fp32_logits(keys, banks, n, d, q, G, scores, (hipStream_t)stream) ? TQ_ERR_DEVICE : TQ_OK;
+}
+
+extern "C" int tq_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return TQ_OK;
+    if (!src || !dst || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15) || (bytes & 15)) return TQ_ERR_ARG;
+    return launch_copy(src, dst, bytes, (hipStream_t)stream) ? TQ_ERR_DEVICE : TQ_OK;
+}
+
+extern "C" const char *tq_status_string(int status) {
+    switch (status) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_ARG: return "invalid argument";
+        case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TQ_ERR_DEVICE: return "device launch failed";
+        case TQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        default: return "unknown status";
+    }
+}

@@ -138,6 +138,25 @@ def encode(prm: Params, keys: np.ndarray):
     return bits, norms, rnorms
 
 
+def encode_trace(prm: Params, keys: np.ndarray):
+    """encode() plus the fp64 values every decision was taken on: z [n, d] (group
+    order, unit variance) and the sketch projections p [n, m]."""
+    sp = prm.spec
+    k = np.ascontiguousarray(keys, dtype=np.float32)
+    n = k.shape[0]
+    npd = n_pad(n)
+    bits = np.zeros((npd // 16, sp.words, 16), np.uint32)
+    norms = np.zeros((npd, sp.ng), np.float32)
+    rnorms = np.zeros(npd, np.float32)
+    z = np.zeros((n, sp.d), np.float64)
+    p = np.zeros((n, max(sp.m, 1)), np.float64)
+    rc = lib().orc_encode_trace(sp.ref(), _p(prm.rot), _p(prm.proj), _p(prm.cent), _p(prm.thr), _p(k),
+                                ctypes.c_long(n), _p(bits), _p(norms), _p(rnorms), _p(z), _p(p))
+    if rc:
+        raise ValueError("orc_encode_trace")
+    return bits, norms, rnorms, z, p[:, : sp.m]
+
+
 def decode(prm: Params, bits: np.ndarray, norms: np.ndarray, n: int) -> np.ndarray:
     sp = prm.spec
     out = np.zeros((n, sp.d), np.float64)

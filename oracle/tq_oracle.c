@@ -257,8 +257,21 @@ static int get_bit(const uint32_t *bits, int W, long key, int word, int bit) {
 /* rot: group rotations concatenated (d_0 x d_0 then d_1 x d_1), fp64.
  * proj: S, m x d float32 (original channel order). cent/thr: per group, 16/15 slots.
  * keys: n x d float32. Writes n_pad keys (zero-vector encodings in the padding). */
+/* As orc_encode, also returning (nullable) the fp64 quantities each decision was taken on:
+ * z_out[key][pos] (unit-variance rotated coordinates, group order) and p_out[key][i]
+ * (sketch projections of the residual), for keys < n. */
+int orc_encode_trace(const orc_cfg *c, const double *rot, const float *proj, const double *cent, const float *thr,
+                     const float *keys, long n, uint32_t *bits, float *norms, float *rnorms, double *z_out,
+                     double *p_out);
+
 int orc_encode(const orc_cfg *c, const double *rot, const float *proj, const double *cent, const float *thr,
                const float *keys, long n, uint32_t *bits, float *norms, float *rnorms) {
+    return orc_encode_trace(c, rot, proj, cent, thr, keys, n, bits, norms, rnorms, NULL, NULL);
+}
+
+int orc_encode_trace(const orc_cfg *c, const double *rot, const float *proj, const double *cent, const float *thr,
+                     const float *keys, long n, uint32_t *bits, float *norms, float *rnorms, double *z_out,
+                     double *p_out) {
     if (cfg_check(c)) return ORC_EARG;
     const int d = c->d, m = c->m, W = cfg_words(c);
     const long n_pad = 16 * ((n + 15) / 16);
@@ -288,6 +301,7 @@ int orc_encode(const orc_cfg *c, const double *rot, const float *proj, const dou
             double coef[1024];
             for (int j = 0; j < dg; ++j) {
                 double z = nu > 0.0 ? sqrt((double)dg) * y[j] / nu : 0.0;
+                if (z_out && key < n) z_out[key * d + off + j] = z;
                 int idx = orc_bucketize((float)z, thr + g * 15, L);
                 for (int p = 0; p < c->gbits[g]; ++p)
                     put_bit(bits, W, key, word0 + p * (dg / 32) + j / 32, j % 32, (idx >> p) & 1);
@@ -313,6 +327,7 @@ int orc_encode(const orc_cfg *c, const double *rot, const float *proj, const dou
             for (int i = 0; i < m; ++i) {
                 double p = 0.0;
                 for (int k = 0; k < d; ++k) p += (double)proj[(long)i * d + k] * r[k];
+                if (p_out && key < n) p_out[key * m + i] = p;
                 put_bit(bits, W, key, word0 + i / 32, i % 32, (float)p >= 0.0f);
             }
         } else if (rnorms) {

@@ -1,0 +1,273 @@
+"""GPU (gfx950 HIP path, through the C ABI) against the CPU oracle.
+
+Sizes the oracle finishes in seconds span many 16-key tiles and a ragged tail;
+the full-size workloads are checked on sampled outputs the oracle computes one
+by one. See tests/parity.py for the tolerances.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import (both_params, check_encode, check_scores, download_bank, groups_of, unpack, upload_bank)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_inner_amd as tq
+
+    return tq
+
+
+def _dev_keys(cfg, keys):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(keys)).cuda()
+    return t.to(torch.bfloat16) if cfg.key_dtype == "bf16" else t
+
+
+def _encode_check(tq, cfg, bits, keys, layer=0, report=None):
+    import torch
+
+    banks, n = keys.shape[0], keys.shape[1]
+    gpu, orc = both_params(cfg, bits, layer)
+    bank = tq.Bank(gpu, banks, n)
+    tq.tq_encode(gpu, _dev_keys(cfg, keys), bank)
+    torch.cuda.synchronize()
+    gb = download_bank(bank)
+    report = {} if report is None else report
+    for b in range(banks):
+        ref = oracle.encode_trace(orc, keys[b])
+        check_encode((gb[0][b], gb[1][b], gb[2][b]), ref, orc, n, report)
+    return gpu, orc, bank, report
+
+
+def _score_check(tq, cfg, bits, keys, q, layer=0):
+    import torch
+
+    banks, n = keys.shape[0], keys.shape[1]
+    gpu, orc = both_params(cfg, bits, layer)
+    refs = [oracle.encode(orc, keys[b]) for b in range(banks)]
+    bank = upload_bank(tq, gpu, np.stack([r[0] for r in refs]), np.stack([r[1] for r in refs]),
+                       np.stack([r[2] for r in refs]), n)
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+    worst = 0.0
+    for b in range(banks):
+        ref = oracle.score(orc, *refs[b], n, q[b])
+        worst = max(worst, check_scores(got[b], ref, f"bank {b}"))
+    return worst
+
+
+# ------------------------------------------------------------------------------------------
+# scorer on oracle-encoded banks (identical bank bytes on both sides)
+# ------------------------------------------------------------------------------------------
+
+def test_score_tiny_full(tq):
+    cfg = workloads.CONFIGS["tiny"]
+    say("score tiny: n=1024 G=16 b=3")
+    keys = workloads.keys(cfg)
+    q = workloads.queries(cfg)
+    say("max err", _score_check(tq, cfg, 3, keys, q))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_score_decode3b_full(tq, bits):
+    cfg = workloads.CONFIGS["decode3b"]
+    say(f"score decode3b: 2 banks x 8192, G=8, b={bits}")
+    keys = workloads.keys(cfg)
+    q = workloads.queries(cfg)
+    say("max err", _score_check(tq, cfg, bits, keys, q))
+
+
+def test_score_longctx_two_groups(tq):
+    cfg = workloads.CONFIGS["longctx"]
+    say("score longctx two groups: 3 banks x 2000, G=4")
+    keys = workloads.keys(cfg, n=2000, banks=[0, 3, 7])
+    q = workloads.queries(cfg, banks=[0, 3, 7])
+    say("max err", _score_check(tq, cfg, 3, keys, q))
+
+
+@pytest.mark.parametrize("n,G", [(1, 1), (15, 3), (16, 4), (17, 5), (33, 16), (1000, 2), (999, 13)])
+def test_score_ragged_shapes(tq, n, G):
+    cfg = workloads.CONFIGS["decode8b"]
+    say(f"score ragged n={n} G={G}")
+    keys = workloads.keys(cfg, n=n, banks=[1, 2])
+    q = workloads.queries(cfg, banks=[1, 2], G=G)
+    _score_check(tq, cfg, 3, keys, q)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_score_other_head_dims(tq, d):
+    import dataclasses
+
+    cfg = dataclasses.replace(workloads.CONFIGS["decode8b"], d=d, m=d, cfg_id=40 + d // 64)
+    say(f"score d={d}")
+    keys = workloads.keys(cfg, n=300, banks=[0])
+    q = workloads.queries(cfg, banks=[0], G=4)
+    _score_check(tq, cfg, 3, keys, q)
+
+
+def test_score_random_banks_full_decode8b_layer(tq):
+    """Full 8B-class layer (64 banks x 32768 keys, G=4) on random bank bytes, in the
+    launch configuration the benchmark uses; sampled pairs against the oracle."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    for bits in (3, 4):
+        say(f"score full layer random bank b={bits}")
+        gpu, orc = both_params(cfg, bits)
+        W, npad, _ = gpu.layout(cfg.tokens)
+        rb, rn, rr = workloads.random_bank(cfg.cfg_id, cfg.banks, npad, W, 1)
+        bank = upload_bank(tq, gpu, rb, rn, rr, cfg.tokens)
+        q = workloads.queries(cfg)
+        got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+        g = np.random.default_rng(bits)
+        for b in g.choice(cfg.banks, 6, replace=False):
+            ki = np.concatenate([g.integers(0, cfg.tokens, 250), [0, cfg.tokens - 1]])
+            qi = g.integers(0, cfg.G, len(ki))
+            ref = oracle.score_pairs(orc, rb[b], rn[b], rr[b], q[b], qi, ki)
+            check_scores(got[b, qi, ki], ref, f"bank {b}")
+
+
+# ------------------------------------------------------------------------------------------
+# encoder against the oracle's encoding of the same keys
+# ------------------------------------------------------------------------------------------
+
+def test_encode_tiny_full(tq):
+    cfg = workloads.CONFIGS["tiny"]
+    say("encode tiny")
+    _, _, _, rep = _encode_check(tq, cfg, 3, workloads.keys(cfg))
+    say("report", rep)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_encode_decode3b_full(tq, bits):
+    cfg = workloads.CONFIGS["decode3b"]
+    say(f"encode decode3b b={bits}")
+    _, _, _, rep = _encode_check(tq, cfg, bits, workloads.keys(cfg))
+    say("report", rep)
+
+
+def test_encode_longctx_two_groups(tq):
+    cfg = workloads.CONFIGS["longctx"]
+    say("encode longctx two groups")
+    _, _, _, rep = _encode_check(tq, cfg, 3, workloads.keys(cfg, n=3000, banks=[0, 5]))
+    say("report", rep)
+
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 100])
+def test_encode_ragged(tq, n):
+    cfg = workloads.CONFIGS["decode8b"]
+    say(f"encode ragged n={n}")
+    _encode_check(tq, cfg, 4, workloads.keys(cfg, n=n, banks=[3, 4, 5]))
+
+
+def test_encode_degenerate_keys(tq):
+    """Zero keys, a key zero in one channel group only, and very large / small norms."""
+    cfg = workloads.CONFIGS["longctx"]
+    keys = workloads.keys(cfg, n=64, banks=[0])
+    keys[0, 3] = 0.0
+    chan = workloads.group_channels(cfg)
+    keys[0, 5, chan[:32]] = 0.0
+    keys[0, 6, chan[32:]] = 0.0
+    keys[0, 7] *= 1024.0
+    keys[0, 8] /= 1024.0
+    say("encode degenerate keys")
+    gpu, orc, bank, _ = _encode_check(tq, cfg, 3, keys)
+    _, _, rr = download_bank(bank)
+    assert rr[0, 3] == 0.0
+
+
+def test_encode_bf16_and_f32_inputs_agree(tq):
+    import torch
+
+    cfg = workloads.CONFIGS["decode3b"]
+    gpu, _ = both_params(cfg, 3)
+    keys = workloads.keys(cfg, n=500)  # bf16-representable values
+    out = []
+    for dt in (torch.bfloat16, torch.float32):
+        bank = tq.Bank(gpu, 2, 500)
+        tq.tq_encode(gpu, torch.from_numpy(keys).cuda().to(dt), bank)
+        out.append(download_bank(bank))
+    for a, b in zip(*out):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_determinism(tq):
+    import torch
+
+    cfg = workloads.CONFIGS["decode3b"]
+    gpu, _ = both_params(cfg, 4)
+    keys = _dev_keys(cfg, workloads.keys(cfg, n=4000))
+    q = torch.from_numpy(workloads.queries(cfg)).cuda()
+    res = []
+    for _ in range(2):
+        bank = tq.Bank(gpu, 2, 4000)
+        tq.tq_encode(gpu, keys, bank)
+        s = tq.tq_score(gpu, bank, q)
+        res.append((download_bank(bank), s.cpu().numpy()))
+    for a, b in zip(res[0][0], res[1][0]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+
+
+def test_end_to_end_against_oracle_pipeline(tq):
+    """GPU encode + GPU score vs oracle encode + oracle score. Codes may differ inside
+    the decision band, so the difference is reported; it must stay rare."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode3b"]
+    keys = workloads.keys(cfg, n=4096)
+    q = workloads.queries(cfg)
+    for bits in (3, 4):
+        gpu, orc = both_params(cfg, bits)
+        bank = tq.Bank(gpu, 2, 4096)
+        tq.tq_encode(gpu, _dev_keys(cfg, keys), bank)
+        got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+        beyond = 0
+        for b in range(2):
+            ref = oracle.score(orc, *oracle.encode(orc, keys[b]), 4096, q[b])
+            err = np.abs(got[b] - ref)
+            beyond += int((err > 1e-4 + 1e-3 * np.abs(ref)).sum())
+        say(f"end-to-end b={bits}: {beyond} of {got.size} scores beyond the score tolerance")
+        assert beyond <= 1e-3 * got.size
+
+
+def test_encode_full_decode8b_layer_sampled(tq):
+    """Full 8B-class layer encoded on the GPU (64 banks x 32768 bf16 keys, drawn on the
+    device); 2048 sampled keys re-encoded by the oracle and compared record by record."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    layer = 31
+    keys = workloads.keys_device(cfg, layer, "cuda")
+    for bits in (3, 4):
+        say(f"encode full layer b={bits}")
+        gpu, orc = both_params(cfg, bits, layer)
+        bank = tq.Bank(gpu, cfg.banks, cfg.tokens)
+        tq.tq_encode(gpu, keys, bank)
+        g = np.random.default_rng(7 + bits)
+        bi = g.integers(0, cfg.banks, 2048)
+        ki = g.integers(0, cfg.tokens, 2048)
+        ki[:2] = [0, cfg.tokens - 1]
+        bt, kt = torch.from_numpy(bi).cuda(), torch.from_numpy(ki).cuda()
+        sk = keys[bt, kt].float().cpu().numpy()
+        gbits = bank.bits[bt, kt // 16, :, kt % 16].cpu().numpy().view(np.uint32)  # [2048, W]
+        gathered = np.ascontiguousarray(gbits.reshape(128, 16, -1).transpose(0, 2, 1))
+        gn = bank.norms[bt, kt].cpu().numpy()
+        gr = bank.rnorms[bt, kt].cpu().numpy()
+        rep = {}
+        check_encode((gathered, gn, gr), oracle.encode_trace(orc, sk), orc, 2048, rep)
+        say("report", rep)

@@ -1,0 +1,177 @@
+"""Host-side checks of libtq.so that need no GPU: exported symbols, the host
+parameter builders against the oracle's independent implementations, bank
+geometry, workspace planning and argument validation (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    from kv_cache_inner_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    import kv_cache_inner_amd as tq
+
+    return tq
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "tq.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol(tq):
+    names = _declared_functions()
+    assert len(names) == 12
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert sorted(tq.EXPORTS) == names
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(tq, bits):
+    c, t, mse = tq.tq_make_codebook(bits)
+    oc, ot, omse, _ = oracle.codebook(bits)
+    np.testing.assert_array_equal(c, oc.astype(np.float32))
+    np.testing.assert_allclose(t, ot.astype(np.float32), atol=1e-7)
+    assert abs(mse - omse) < 1e-12
+    np.testing.assert_array_equal(c, -c[::-1])
+    np.testing.assert_array_equal(t, -t[::-1])
+
+
+@pytest.mark.parametrize("d", [32, 96, 128, 768])
+def test_rotation_matches_oracle(tq, d):
+    G = np.random.default_rng(1000 + d).standard_normal((d, d)).astype(np.float32)
+    R = tq.tq_make_rotation(G)
+    Ro = oracle.rotation(G)
+    assert np.abs(R.astype(np.float64) - Ro).max() < 1e-6
+    assert np.abs(R.astype(np.float64) @ R.T.astype(np.float64) - np.eye(d)).max() < 1e-5
+
+
+def test_rotation_rejects_rank_deficient(tq):
+    G = np.ones((32, 32), np.float32)
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_make_rotation(G)
+    assert e.value.code == tq.TQ_ERR_ARG
+
+
+def _params(tq, d=128, m=128, groups=((128, 2),), codebooks=None):
+    return tq.Params(d, m, groups, rot=None, proj=None, codebooks=codebooks)
+
+
+class _FakePtr:
+    def __init__(self, v):
+        self.v = v
+
+    def data_ptr(self):
+        return self.v
+
+
+def _with_fake_ptrs(tq, **kw):
+    p = _params(tq, **kw)
+    p.struct.rot = 0x10000
+    p.struct.proj = 0x20000
+    return p
+
+
+@pytest.mark.parametrize("groups,m,W,bpk", [
+    (((128, 2),), 128, 12, 56),     # d=128, b=3 (2-bit codebook + sketch)
+    (((128, 3),), 128, 16, 72),     # d=128, b=4
+    (((32, 2), (96, 1)), 128, 9, 48),  # two groups, 2.25 bits/channel of codes+sketch
+    (((768, 1),), 768, 48, 200),    # search, b=2
+    (((768, 3),), 768, 96, 392),    # search, b=4
+])
+def test_bank_geometry(tq, groups, m, W, bpk):
+    d = sum(g[0] for g in groups)
+    p = _with_fake_ptrs(tq, d=d, m=m, groups=groups)
+    w, npad, b = p.layout(1000)
+    assert (w, npad, b) == (W, 1008, bpk)
+    assert p.layout(0)[1] == 0 and p.layout(16)[1] == 16 and p.layout(17)[1] == 32
+
+
+def test_workspace_sizes(tq):
+    p = _with_fake_ptrs(tq)
+    assert p.workspace_bytes(tq.TQ_OP_ENCODE, 4, 100) == 128 * 128 * 4
+    s = p.workspace_bytes(tq.TQ_OP_SCORE, 64, 32768, 4)
+    assert s > 0 and s % 256 == 0
+    assert p.workspace_bytes(tq.TQ_OP_SCORE, 64, 32768, 0) == 0
+    assert p.workspace_bytes(tq.TQ_OP_TOPK, 1, 1000, 16, 10) > p.workspace_bytes(tq.TQ_OP_SCORE, 1, 1000, 16)
+    assert p.workspace_bytes(tq.TQ_OP_TOPK, 1, 1000, 16, 65) == 0
+    # a valid shape without a compiled scorer layout
+    q = _with_fake_ptrs(tq, d=160, m=128, groups=((160, 2),))
+    assert q.workspace_bytes(tq.TQ_OP_SCORE, 1, 100, 4) == 0
+
+
+def _rc(fn, *a):
+    return fn(*a)
+
+
+def test_argument_validation_returns_before_any_launch(tq):
+    L = tq._lib.lib()
+    good = _with_fake_ptrs(tq)
+    bank = tq.tq_bank(0x30000, 0x40000, 0x50000)
+    nullbank = tq.tq_bank(None, None, None)
+    # invalid parameter structs
+    def patched(**fields):
+        p = _with_fake_ptrs(tq)
+        for k, v in fields.items():
+            if k in ("group_dim", "group_bits"):
+                getattr(p.struct, k)[0] = v
+            else:
+                setattr(p.struct, k, v)
+        return p
+
+    for p in [patched(d=100, group_dim=100), patched(m=100), patched(m=0), patched(group_bits=4),
+              patched(group_bits=0), patched(group_dim=64), patched(n_groups=3), patched(d=2048, group_dim=2048)]:
+        assert L.tq_encode(p.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+        assert L.tq_score(p.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
+    # missing matrices
+    p = _params(tq)
+    assert L.tq_bank_layout(p.ref, 10, None, None, None) == tq.TQ_ERR_ARG
+    # asymmetric codebook: valid but unsupported by the kernels
+    c, t, _ = tq.tq_make_codebook(2)
+    c2 = c.copy()
+    c2[0] -= 0.01
+    asym = _params(tq, codebooks=[(c2, t)])
+    asym.struct.rot, asym.struct.proj = 0x10000, 0x20000
+    assert L.tq_bank_layout(asym.ref, 10, None, None, None) == tq.TQ_ERR_UNSUPPORTED
+    # thresholds outside their cells
+    t2 = t.copy()
+    t2[0] = c[0] - 1
+    bad = _params(tq, codebooks=[(c, t2)])
+    bad.struct.rot, bad.struct.proj = 0x10000, 0x20000
+    assert L.tq_bank_layout(bad.ref, 10, None, None, None) == tq.TQ_ERR_ARG
+    # null buffers, negative sizes, bad dtype, bad k, workspace too small
+    assert L.tq_encode(good.ref, None, 0, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_encode(good.ref, 0x1000, 0, 1, 10, ctypes.byref(nullbank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_encode(good.ref, 0x1000, 7, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_encode(good.ref, 0x1000, 0, -1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_encode(good.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2000, 16, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_encode(good.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2001, 1 << 20, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, None, 4, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 0, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 8, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 11, 0x2000, 0x3000, 0x4000, 1 << 20,
+                     None) == tq.TQ_ERR_ARG
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 0, 0x2000, 0x3000, 0x4000, 1 << 20,
+                     None) == tq.TQ_ERR_ARG
+    assert L.tq_fp32_logits(None, 1, 10, 128, 0x1000, 4, 0x2000, None) == tq.TQ_ERR_ARG
+    assert L.tq_copy(0x1001, 0x2000, 64, None) == tq.TQ_ERR_ARG
+    # empty inputs are valid no-ops
+    assert L.tq_encode(good.ref, None, 0, 0, 10, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
+    assert L.tq_encode(good.ref, None, 0, 3, 0, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
+    assert L.tq_score(good.ref, ctypes.byref(nullbank), 3, 0, None, 4, None, None, 0, None) == tq.TQ_OK
+    assert L.tq_copy(None, None, 0, None) == tq.TQ_OK
+    for code in (0, -1, -2, -3, -4, 9):
+        assert isinstance(tq.tq_status_string(code), str)
