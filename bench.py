@@ -1,0 +1,340 @@
+"""Benchmark of the packed-key scorer on the 8B-class decode workload.
+
+One step = one decode step of the whole model's attention logits: for each of
+32 layers, tq_score (query preparation + the packed-key scorer) of the batch's
+queries against that layer's packed keys: batch 8, 32768-token context, 8 kv
+heads, 32 query heads (G = 4 per bank), d = 128, b = 3 (2-bit codebook + 1-bit
+sketch, m = 128). Value = estimated inner products per second.
+
+The same run also times the encoder over all 32 layers (keys/s), the b = 4
+variant of the sweep, the fp32 unquantized-keys logits kernel on the same
+shapes, and the CPU oracle on a bounded sample (rank 0). Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+METRIC = "packed-key inner products/sec + HBM GB/s (% peak), d=128 b=3, 32K ctx decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_inner_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters_for(kernel: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}|{workload}")
+    except ValueError:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def groups_of(cfg, bits):
+    """(d_g, codebook bits) per channel group for a total budget of `bits` (1 bit is the sketch)."""
+    return [(cfg.d, bits - 1)] if cfg.groups is None else [(dg, b - 1) for dg, b in cfg.groups]
+
+
+def params_for(tq, cfg, bits, device):
+    import workloads
+
+    groups = groups_of(cfg, bits)
+    gauss = workloads.rotation_gaussians(cfg.cfg_id, [g[0] for g in groups])
+    S = workloads.projection(cfg.cfg_id, cfg.m, cfg.d)
+    return tq.make_params(cfg.d, cfg.m, groups, gauss, S, workloads.group_channels(cfg), device)
+
+
+class Sweep:
+    """Packed banks of all layers for one bit budget, plus per-layer queries."""
+
+    def __init__(self, tq, cfg, bits, layers, device, time_encode=False):
+        import torch
+
+        self.cfg, self.bits, self.layers = cfg, bits, layers
+        self.params = params_for(tq, cfg, bits, device)
+        self.banks, self.queries = [], []
+        W, npad, bpk = self.params.layout(cfg.tokens)
+        self.bytes_per_key = bpk
+        enc_events = []
+        enc_ws = torch.empty(self.params.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), dtype=torch.uint8,
+                             device=device)
+        import workloads
+
+        for layer in range(layers):
+            keys = workloads.keys_device(cfg, layer, device)
+            bank = tq.Bank(self.params, cfg.banks, cfg.tokens, device)
+            if time_encode:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            tq.tq_encode(self.params, keys, bank, workspace=enc_ws)
+            if time_encode:
+                e1.record()
+                enc_events.append((e0, e1))
+            self.banks.append(bank)
+            self.queries.append(workloads.queries_device(cfg, layer, device))
+            del keys
+        torch.cuda.synchronize()
+        self.encode_ms = [a.elapsed_time(b) for a, b in enc_events]
+        self.ws = tq.score_workspace(self.params, self.banks[0], cfg.G)
+        self.scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+
+    def step(self, tq, events=None):
+        """One decode step: per layer, one tq_score call (query preparation fused into the
+        packed-key scorer: a single kernel launch). The C entry point is called with
+        pre-marshalled arguments so that host-side Python overhead stays below the GPU time
+        per layer."""
+        import torch
+
+        if not hasattr(self, "_calls"):
+            lib = tq._lib.lib()
+            stream = torch.cuda.current_stream().cuda_stream
+            ws, wsn = self.ws.data_ptr(), self.ws.numel()
+            self._calls = [(lib.tq_score, (self.params.ref, self.banks[l].ref, self.cfg.banks, self.cfg.tokens,
+                                           self.queries[l].data_ptr(), self.cfg.G, self.scores.data_ptr(), ws, wsn,
+                                           stream))
+                           for l in range(self.layers)]
+        for score, sa in self._calls:
+            if events is not None:
+                e0, e1 = events.pop()
+                e0.record()
+            if score(*sa):
+                raise RuntimeError("tq_score failed")
+            if events is not None:
+                e1.record()
+                events.done.append((e0, e1))
+
+
+class EventPool(list):
+    """Pre-created timing events (creating them inside the timed loop costs host time)."""
+
+    def __init__(self, n):
+        import torch
+
+        super().__init__((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                         for _ in range(n))
+        self.done = []
+
+
+def timed(fn, steps, warmup, launches_per_step):
+    import torch
+
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    events = EventPool(steps * launches_per_step)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in events.done]
+    return wall, kern_ms
+
+
+def cpu_baseline(cfg, bits, n_keys, banks):
+    """The oracle (fp64, OpenMP) on a bounded sample: it encodes `banks` banks of n_keys
+    keys of layer 0 and scores them with the layer's queries."""
+    import oracle
+    import workloads
+    groups = groups_of(cfg, bits)
+    orc = oracle.Params(oracle.Spec(cfg.d, cfg.m, groups, workloads.group_channels(cfg)),
+                        workloads.rotation_gaussians(cfg.cfg_id, [g[0] for g in groups]),
+                        workloads.projection(cfg.cfg_id, cfg.m, cfg.d))
+    keys = workloads.keys(cfg, 0, n=n_keys, banks=range(banks))
+    q = workloads.queries(cfg, 0, banks=range(banks))
+    t0 = time.perf_counter()
+    encs = [oracle.encode(orc, keys[b]) for b in range(banks)]
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for b in range(banks):
+        oracle.score(orc, *encs[b], n_keys, q[b])
+    t_score = time.perf_counter() - t0
+    pairs = banks * n_keys * cfg.G
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": pairs / t_score,
+        "unit": "pairs/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{banks} banks x {n_keys} keys x G={cfg.G} of the 8B-class layer 0, b={bits}; "
+                  f"score timed {t_score:.2f}s, oracle encode of the same keys {t_enc:.2f}s "
+                  f"({banks * n_keys / t_enc:.3g} keys/s)",
+        "encode_keys_per_s": banks * n_keys / t_enc,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline sweep")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (calibrates the HBM traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU only: every bank is independent, so more "
+                                   "GPUs would each run this same single-GPU sweep on their own banks; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_inner_amd as tq
+    import workloads
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = workloads.CONFIGS["decode8b"]
+    L = args.layers
+    if args.copy_mib:
+        nbytes = args.copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        tq.tq_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log(f"encode + pack {L} layers (b=3)")
+    sw3 = Sweep(tq, cfg, 3, L, device, time_encode=True)
+    keys_total = cfg.banks * cfg.tokens * L
+    enc_ms = sum(sw3.encode_ms)
+    log(f"encode: {enc_ms:.2f} ms for {keys_total} keys")
+
+    log("timed sweep b=3")
+    wall, kern_ms = timed(lambda ev: sw3.step(tq, ev), args.steps, args.warmup, L)
+    ms_per_step = 1e3 * wall / args.steps
+    pairs_per_step = cfg.banks * cfg.tokens * cfg.G * L
+    value = pairs_per_step / (wall / args.steps)
+    bytes_per_launch = cfg.banks * cfg.tokens * (sw3.bytes_per_key + 4 * cfg.G)
+    kavg = float(np.mean(kern_ms))
+    achieved = bytes_per_launch / (kavg * 1e-3) / 1e9
+    step_gbps = bytes_per_launch * L / (wall / args.steps) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode8b: 32 layers x batch 8 x 8 kv heads x 32768 keys, G=4 queries per kv head, "
+                        "d=128, b=3 (2-bit codebook + 1-bit sign sketch, m=128), bf16 keys N(0,1) x "
+                        "lognormal(0,0.5) channel scales",
+            "layers": L, "banks_per_layer": cfg.banks, "keys_per_bank": cfg.tokens, "G": cfg.G, "d": cfg.d,
+            "bits": 3, "bytes_per_key": sw3.bytes_per_key,
+        },
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_fused_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": counters_for("score_fused_kernel", "decode8b_b3"),
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "avg_launch_ms": kavg,
+            "launches": len(kern_ms),
+        },
+        "encode": {
+            "keys_per_s": keys_total / (enc_ms * 1e-3),
+            "ms_total": enc_ms,
+            "tflops": keys_total * 2 * cfg.d * (cfg.d + cfg.m) / (enc_ms * 1e-3) / 1e12,
+            "mfma_fp32_frac": keys_total * 2 * cfg.d * (cfg.d + cfg.m) / (enc_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        },
+    }
+    del sw3
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        log("b=4 sweep")
+        sw4 = Sweep(tq, cfg, 4, L, device)
+        wall4, kern4 = timed(lambda ev: sw4.step(tq, ev), max(args.steps // 2, 1), 2, L)
+        b4_bytes = cfg.banks * cfg.tokens * (sw4.bytes_per_key + 4 * cfg.G)
+        out["b4"] = {
+            "value": pairs_per_step / (wall4 / max(args.steps // 2, 1)),
+            "unit": "pairs/s",
+            "bytes_per_key": sw4.bytes_per_key,
+            "kernel_gbps": b4_bytes / (np.mean(kern4) * 1e-3) / 1e9,
+            "kernel_frac": b4_bytes / (np.mean(kern4) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        }
+        del sw4
+        torch.cuda.empty_cache()
+
+        log("fp32 unquantized-keys comparator")
+        nfp = 4  # distinct fp32 layers (4.3 GB, far beyond the 256 MB last-level cache), cycled
+        kf = [workloads.keys_device(cfg, l, device, dtype=torch.float32) for l in range(nfp)]
+        qf = [workloads.queries_device(cfg, l, device) for l in range(nfp)]
+        sf = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+
+        def fp32_step(ev):
+            for layer in range(L):
+                if ev is not None:
+                    e0, e1 = ev.pop()
+                    e0.record()
+                tq.tq_fp32_logits(kf[layer % nfp], qf[layer % nfp], sf)
+                if ev is not None:
+                    e1.record()
+                    ev.done.append((e0, e1))
+
+        wallf, kernf = timed(fp32_step, max(args.steps // 4, 1), 1, L)
+        fbytes = cfg.banks * cfg.tokens * (4 * cfg.d + 4 * cfg.G)
+        out["fp32_comparator"] = {
+            "value": pairs_per_step / (wallf / max(args.steps // 4, 1)),
+            "unit": "pairs/s",
+            "kernel_gbps": fbytes / (np.mean(kernf) * 1e-3) / 1e9,
+            "speedup_of_packed_b3": (np.mean(kernf)) / kavg,
+            "context": "the pages quote up to 8x for 4-bit keys vs 32-bit keys on H100",
+        }
+        del kf
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(cfg, 3, 32768, 2)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -140,6 +140,30 @@ struct Layout {
         return f;
     }
     static constexpr int NF = count_frags();
+
+    // bit positions feeding estimator term c (bounds its integer limb sums)
+    static constexpr int class_positions(int c) {
+        int n = 0;
+        for (int dw = 0; dw < DW; ++dw)
+            if (dword(dw).cls == c) n += 32;
+        return n;
+    }
+
+    // inverse of frag_index: quad, half and class of fragment f
+    static constexpr int frag_field(int f, int which) {
+        int k = 0;
+        for (int q = 0; q < NQ; ++q)
+            for (int h = 0; h < 2; ++h)
+                for (int c = 0; c < NCLS; ++c)
+                    if (quad_has(q, c)) {
+                        if (k == f) return which == 0 ? q : which == 1 ? h : c;
+                        ++k;
+                    }
+        return -1;
+    }
+    static constexpr int frag_q(int f) { return frag_field(f, 0); }
+    static constexpr int frag_h(int f) { return frag_field(f, 1); }
+    static constexpr int frag_c(int f) { return frag_field(f, 2); }
 };
 
 }  // namespace tq

@@ -310,7 +310,7 @@ extern "C" int tq_prepare_queries(const tq_params *p, const float *q, int64_t ba
         if (banks * pl.Gpad > INT32_MAX) return (int)TQ_ERR_UNSUPPORTED;
         int8_t *frags = (int8_t *)workspace;
         double *consts = (double *)((char *)workspace + pl.const_off);
-        hipLaunchKernelGGL(qprep_kernel<L>, dim3((unsigned)(banks * pl.Gpad)), dim3(256), 0, (hipStream_t)stream, q,
+        hipLaunchKernelGGL(qprep_kernel<L>, dim3((unsigned)(banks * pl.Gpad / 4)), dim3(1024), 0, (hipStream_t)stream, q,
                            p->rot, p->proj, p->group_chan, prep_args(p), (int)G, pl.Gpad, frags, consts);
         return launch_status();
     });
@@ -324,9 +324,24 @@ static ScoreScale score_scale(const tq_params *p) {
     return s;
 }
 
+// tiles per batch in the scorer: fewer when more registers hold operands
+template <class L, int RT>
+constexpr int score_tb() {
+    return (RT == 1 && L::NG == 1) ? 4 : (RT <= 2 ? 2 : 1);
+}
+
+// the decode scorers keep RT x NF operand fragments (4 VGPRs each) in registers
+template <class L, int RT>
+constexpr bool vgpr_operands_fit() {
+    return RT * L::NF <= 40;
+}
+
 template <class L, int RT>
 static int launch_score(const tq_bank *in, int64_t banks, int64_t n, int32_t G, const PrepPlan &pl, const void *ws,
                         float *scores, const ScoreScale &sc, hipStream_t st) {
+    if constexpr (!vgpr_operands_fit<L, RT>()) {
+        return TQ_ERR_UNSUPPORTED;
+    } else {
     const int64_t n_tiles = (n + 15) / 16;
     const int64_t target_waves = 256 * 16;
     int64_t tpw = (banks * n_tiles + target_waves - 1) / target_waves;
@@ -336,10 +351,43 @@ static int launch_score(const tq_bank *in, int64_t banks, int64_t n, int32_t G, 
     if ((waves + 3) / 4 > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     const int8_t *frags = (const int8_t *)ws;
     const double *consts = (const double *)((const char *)ws + pl.const_off);
-    hipLaunchKernelGGL((score_kernel<L, RT>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, in->bits, in->norms,
-                       in->rnorms, frags, consts, scores, (int)banks, (long)n, (int)n_tiles, (int)G, pl.Gpad, (int)tpw,
-                       (int)wpb, sc);
+    hipLaunchKernelGGL((score_kernel<L, RT, score_tb<L, RT>()>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                       in->bits, in->norms, in->rnorms, frags, consts, scores, (int)banks, (long)n, (int)n_tiles, (int)G,
+                       pl.Gpad, (int)tpw, (int)wpb, sc);
     return launch_status();
+    }
+}
+
+// Fused query preparation + scoring (one launch). Work-groups of 16 waves, about one per
+// compute unit, each owning a contiguous range of one bank's tiles.
+template <class L, int RT>
+static constexpr bool fused_fits() {
+    // LDS for the prologue, and operand registers within the per-wave budget of the
+    // work-group size (16 waves: 128 VGPRs; 8 waves: 256)
+    return sizeof(FusedLds<L, RT>) <= 160 * 1024 && (RT == 1 ? L::NF <= 10 : RT * L::NF <= 24);
+}
+
+template <class L, int RT>
+static int launch_fused(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
+                        float *scores, hipStream_t st) {
+    if constexpr (!fused_fits<L, RT>()) {
+        return TQ_ERR_UNSUPPORTED;
+    } else {
+        const int64_t n_tiles = (n + 15) / 16;
+        int64_t wpb = (256 + banks - 1) / banks;                // aim at one work-group per compute unit
+        constexpr int WAVES = fused_waves<RT>();
+        const int64_t max_wpb = (n_tiles + WAVES - 1) / WAVES;  // at least a tile per wave
+        if (wpb > max_wpb) wpb = max_wpb;
+        if (wpb < 1) wpb = 1;
+        const int64_t tpw = (n_tiles + wpb - 1) / wpb;
+        wpb = (n_tiles + tpw - 1) / tpw;
+        if (banks * wpb > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((score_fused_kernel<L, RT, score_tb<L, RT>()>), dim3((unsigned)(banks * wpb)),
+                           dim3(WAVES * 64), 0, st, in->bits, in->norms, in->rnorms, q, p->rot, p->proj,
+                           p->group_chan, prep_args(p), scores, (int)banks, (long)n, (int)n_tiles, (int)G, (int)wpb,
+                           (int)tpw, score_scale(p));
+        return launch_status();
+    }
 }
 
 extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
@@ -373,6 +421,18 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q) return TQ_ERR_ARG;
     if (G > 16) return TQ_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    rc = with_layout(p, [&](auto l) {
+        using L = decltype(l);
+        switch ((G + 3) / 4) {
+            case 1: return launch_fused<L, 1>(p, in, banks, n, q, G, scores, st);
+            case 2: return launch_fused<L, 2>(p, in, banks, n, q, G, scores, st);
+            case 3: return launch_fused<L, 3>(p, in, banks, n, q, G, scores, st);
+            default: return launch_fused<L, 4>(p, in, banks, n, q, G, scores, st);
+        }
+    });
+    if (rc != TQ_ERR_UNSUPPORTED) return rc;
+    // layouts too large for the fused prologue: prepare into the workspace, then score
     if ((rc = tq_prepare_queries(p, q, banks, G, workspace, ws_bytes, stream))) return rc;
     return tq_score_prepared(p, in, banks, n, G, workspace, scores, stream);
 }

@@ -161,7 +161,8 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert L.tq_encode(good.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2001, 1 << 20, None) == tq.TQ_ERR_WORKSPACE
     assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, None, 4, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
     assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 0, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
-    assert L.tq_score(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 8, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_prepare_queries(good.ref, 0x1000, 1, 4, 0x3000, 8, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_prepare_queries(good.ref, 0x1000, 1, 4, 0x3001, 1 << 20, None) == tq.TQ_ERR_WORKSPACE
     assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 11, 0x2000, 0x3000, 0x4000, 1 << 20,
                      None) == tq.TQ_ERR_ARG
     assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 0, 0x2000, 0x3000, 0x4000, 1 << 20,
