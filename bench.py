@@ -161,35 +161,41 @@ def timed(fn, steps, warmup, launches_per_step):
     return wall, kern_ms
 
 
-def cpu_baseline(cfg, bits, n_keys, banks):
-    """The oracle (fp64, OpenMP) on a bounded sample: it encodes `banks` banks of n_keys
-    keys of layer 0 and scores them with the layer's queries."""
+def cpu_baseline(cfg, bits, banks, layers):
+    """The oracle (fp64, OpenMP) on a bounded sample of the sweep: it encodes `banks`
+    banks of layer 0 once, then scores them with the queries of `layers` layers, so
+    the scored pair count equals that of a sweep of `layers` layers over `banks`
+    banks (layer 0's keys stand in for every layer's)."""
     import oracle
     import workloads
     groups = groups_of(cfg, bits)
     orc = oracle.Params(oracle.Spec(cfg.d, cfg.m, groups, workloads.group_channels(cfg)),
                         workloads.rotation_gaussians(cfg.cfg_id, [g[0] for g in groups]),
                         workloads.projection(cfg.cfg_id, cfg.m, cfg.d))
-    keys = workloads.keys(cfg, 0, n=n_keys, banks=range(banks))
-    q = workloads.queries(cfg, 0, banks=range(banks))
+    n = cfg.tokens
+    keys = workloads.keys(cfg, 0, banks=range(banks))
     t0 = time.perf_counter()
     encs = [oracle.encode(orc, keys[b]) for b in range(banks)]
     t_enc = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for b in range(banks):
-        oracle.score(orc, *encs[b], n_keys, q[b])
-    t_score = time.perf_counter() - t0
-    pairs = banks * n_keys * cfg.G
+    del keys
+    t_score = 0.0
+    for layer in range(layers):
+        q = workloads.queries(cfg, layer, banks=range(banks))
+        t0 = time.perf_counter()
+        for b in range(banks):
+            oracle.score(orc, *encs[b], n, q[b])
+        t_score += time.perf_counter() - t0
+    pairs = banks * n * cfg.G * layers
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
         "value": pairs / t_score,
         "unit": "pairs/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{banks} banks x {n_keys} keys x G={cfg.G} of the 8B-class layer 0, b={bits}; "
-                  f"score timed {t_score:.2f}s, oracle encode of the same keys {t_enc:.2f}s "
-                  f"({banks * n_keys / t_enc:.3g} keys/s)",
-        "encode_keys_per_s": banks * n_keys / t_enc,
+        "sample": f"{banks} banks x {n} keys of the 8B-class layer 0 (b={bits}) encoded once, scored against "
+                  f"G={cfg.G} queries of each of {layers} layers ({pairs} pairs, score {t_score:.1f}s); "
+                  f"oracle encode of those keys {t_enc:.1f}s ({banks * n / t_enc:.3g} keys/s)",
+        "encode_keys_per_s": banks * n / t_enc,
     }
 
 
@@ -332,7 +338,7 @@ def main():
 
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(cfg, 3, 32768, 2)
+        out["cpu_baseline"] = cpu_baseline(cfg, 3, cfg.banks, L)
     print(json.dumps(out))
 
 
