@@ -390,6 +390,35 @@ static int launch_fused(const tq_params *p, const tq_bank *in, int64_t banks, in
     }
 }
 
+// Ring-staged fused scorer (G <= 4): needs a ring of at least 4 tiles per wave next to the
+// prologue's LDS, and the operand registers of one row tile.
+template <class L>
+static constexpr bool ring_fits() {
+    return ring_slots<L>() >= 4 && L::NF <= 10 && RingTile<L>::LOADS * (ring_slots<L>() - 1) <= 63;
+}
+
+template <class L>
+static int launch_ring(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
+                       float *scores, hipStream_t st) {
+    if constexpr (!ring_fits<L>()) {
+        return TQ_ERR_UNSUPPORTED;
+    } else {
+        const int64_t n_tiles = (n + 15) / 16;
+        int64_t wpb = (256 + banks - 1) / banks;  // aim at one work-group per compute unit
+        const int64_t max_wpb = (n_tiles + RING_WAVES - 1) / RING_WAVES;
+        if (wpb > max_wpb) wpb = max_wpb;
+        if (wpb < 1) wpb = 1;
+        const int64_t tpw = (n_tiles + wpb - 1) / wpb;
+        wpb = (n_tiles + tpw - 1) / tpw;
+        if (banks * wpb > INT32_MAX || 4 * n > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((score_ring_kernel<L, ring_slots<L>()>), dim3((unsigned)(banks * wpb)),
+                           dim3(RING_WAVES * 64), 0, st, in->bits, in->norms, in->rnorms, q, p->rot, p->proj,
+                           p->group_chan, prep_args(p), scores, (int)banks, (long)n, (int)n_tiles, (int)G, (int)wpb,
+                           (int)tpw, score_scale(p));
+        return launch_status();
+    }
+}
+
 extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
                                  const void *workspace, float *scores, void *stream) {
     int rc = check_params(p);
@@ -425,7 +454,11 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
     rc = with_layout(p, [&](auto l) {
         using L = decltype(l);
         switch ((G + 3) / 4) {
-            case 1: return launch_fused<L, 1>(p, in, banks, n, q, G, scores, st);
+            case 1: {
+                // four queries per bank: the ring-staged scorer where it fits
+                const int r = G == 4 ? launch_ring<L>(p, in, banks, n, q, G, scores, st) : TQ_ERR_UNSUPPORTED;
+                return r != TQ_ERR_UNSUPPORTED ? r : launch_fused<L, 1>(p, in, banks, n, q, G, scores, st);
+            }
             case 2: return launch_fused<L, 2>(p, in, banks, n, q, G, scores, st);
             case 3: return launch_fused<L, 3>(p, in, banks, n, q, G, scores, st);
             default: return launch_fused<L, 4>(p, in, banks, n, q, G, scores, st);

@@ -15,6 +15,8 @@
 #pragma once
 #include <math.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_layout.h"
 
@@ -55,35 +57,24 @@ struct PrepScratch {
     int F[4 * RT][L::NCLS];
 };
 
-template <class L, int RT, int NT>
-__device__ __forceinline__ void prep_operands(int tid, const float *__restrict__ q, long bank, int G, int q0,
-                                              const float *__restrict__ rot, const float *__restrict__ proj,
-                                              const int *__restrict__ chan, const PrepArgs &pa,
-                                              PrepScratch<L, RT> &ps, int8_t *frag_out, double *const_out) {
-    using PS = PrepScratch<L, RT>;
-    constexpr int NQ4 = 4 * RT;
-    constexpr int NR = PS::NR, CPR = PS::CPR, RB = PS::RB;
-    constexpr int CH = L::D / CPR;  // columns per chunk
-    static_assert(CH % 4 == 0 && 64 % CPR == 0, "bad chunking");
-    static_assert(L::D0 % RB == 0 && L::D % RB == 0, "row blocks must not straddle estimator terms");
-    const int lane = tid & 63, wv = tid / 64;
-    for (int e = tid; e < NQ4 * L::D; e += NT) {
-        const int qq = e / L::D, c = e % L::D, gq = q0 + qq;
-        const float *qrow = q + ((size_t)bank * G + gq) * L::D;
-        ps.qv[c][qq] = gq < G ? qrow[c] : 0.0f;
-        ps.qg[c][qq] = gq < G ? qrow[chan ? chan[c] : c] : 0.0f;
-    }
-    __syncthreads();
-    // Items (query quad, row, part). Part p of a row takes the float4 columns p, p+CPR, ...
-    // so that the CPR lanes of a row read contiguous 16*CPR-byte runs; all loads of an item
-    // are issued before its arithmetic. Parts of a row sit in adjacent lanes, rows of a
-    // wave form one row block; both are reduced with shuffles in a fixed order.
-    for (int it = tid; it < NR * RT * CPR; it += NT) {
-        const int part = it % CPR, item = it / CPR;
-        const int r = item % NR, qb = 4 * (item / NR);
-        const float *row;
-        int K, off = 0;
-        const bool rotated = r < L::D;
+// One GEMV item of the query preparation: (row tile, matrix row, part). Part p of a row
+// takes the float4 columns p, p+CPR, ... so that the CPR lanes of a row read contiguous
+// 16*CPR-byte runs.
+template <class L, int RT>
+struct PrepItem {
+    static constexpr int NR = PrepScratch<L, RT>::NR, CPR = PrepScratch<L, RT>::CPR;
+    static constexpr int CH = L::D / CPR;  // columns per chunk
+    const float *row;
+    int K, off, part, r, qb;
+    bool rotated;
+
+    __device__ __forceinline__ PrepItem(int it, const float *__restrict__ rot, const float *__restrict__ proj) {
+        part = it % CPR;
+        const int item = it / CPR;
+        r = item % NR;
+        qb = 4 * (item / NR);
+        rotated = r < L::D;
+        off = 0;
         if (rotated) {
             const int g = r < L::D0 ? 0 : 1;
             off = g ? L::D0 : 0;
@@ -93,20 +84,128 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
             K = L::D;
             row = proj + (size_t)(r - L::D) * L::D;
         }
-        const float(*src)[NQ4] = rotated ? ps.qg + off : ps.qv;  // operand columns of this row
+    }
+
+    __device__ __forceinline__ void load(f32x4 (&m)[CH / 4]) const {
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) {
+            const int k = 4 * (i * CPR + part);
+            m[i] = k < K ? *reinterpret_cast<const f32x4 *>(row + k) : f32x4{0, 0, 0, 0};
+        }
+    }
+};
+
+// The prologue's global reads that a thread can request up front: its first query
+// element and the matrix chunks of its first PRE GEMV items (items tid, tid + NT, ...).
+// Issuing them before any other vector-memory traffic lets the later waits on them ignore
+// that traffic (loads complete in issue order).
+template <class L, int RT, int NT>
+struct PrepRegs {
+    static constexpr int ITEMS = PrepItem<L, RT>::NR * RT * PrepItem<L, RT>::CPR;
+    static constexpr int PER = (ITEMS + NT - 1) / NT;  // items per thread
+    static constexpr int PRE = PER < 2 ? PER : 2;      // of which preloaded (register budget)
+    float qv, qg;
+    f32x4 m[PRE][PrepItem<L, RT>::CH / 4];
+};
+
+template <class L, int RT, int NT>
+__device__ __forceinline__ void prep_load(PrepRegs<L, RT, NT> &pr, int tid, const float *__restrict__ q, long bank,
+                                          int G, int q0, const float *__restrict__ rot,
+                                          const float *__restrict__ proj, const int *__restrict__ chan) {
+    using PR = PrepRegs<L, RT, NT>;
+    constexpr int NQ4 = 4 * RT;
+    pr.qv = pr.qg = 0.0f;
+    if (tid < NQ4 * L::D) {
+        const int qq = tid / L::D, c = tid % L::D, gq = q0 + qq;
+        const float *qrow = q + ((size_t)bank * G + gq) * L::D;
+        if (gq < G) {
+            pr.qv = qrow[c];
+            pr.qg = chan ? qrow[chan[c]] : pr.qv;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PR::PRE; ++k)
+        if (tid + k * NT < PR::ITEMS) PrepItem<L, RT>(tid + k * NT, rot, proj).load(pr.m[k]);
+}
+
+// Work-group barrier over LDS traffic only: it waits for this wave's LDS operations but not
+// for its vector-memory loads, so direct-to-LDS loads issued earlier stay in flight (a
+// __syncthreads() would drain them: it orders them as pending LDS writes). Only for code
+// whose cross-wave communication goes through ordinary LDS reads and writes.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool LDS_ONLY>
+__device__ __forceinline__ void prep_barrier() {
+    if constexpr (LDS_ONLY)
+        lds_barrier();
+    else
+        __syncthreads();
+}
+
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// The staging and the GEMV use NT threads; the exponent and fragment phases use the
+// threads below NT_TAIL whose tail_worker is set, the others only take part in the
+// barriers. `after_gemv` runs in every thread right after the barrier that ends the GEMV,
+// when no thread reads the query staging or the matrix chunks any more.
+template <class L, int RT, int NT, bool LDS_ONLY = false, int NT_TAIL = NT, class Hook = NoHook>
+__device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int tid, const float *__restrict__ q, long bank,
+                                            int G, int q0, const float *__restrict__ rot,
+                                            const float *__restrict__ proj, const int *__restrict__ chan,
+                                            const PrepArgs &pa, PrepScratch<L, RT> &ps, int8_t *frag_out,
+                                            double *const_out, Hook after_gemv = Hook{},
+                                            bool tail_worker = true) {
+    using PS = PrepScratch<L, RT>;
+    using PI = PrepItem<L, RT>;
+    constexpr int NQ4 = 4 * RT;
+    constexpr int NR = PS::NR, CPR = PS::CPR, RB = PS::RB;
+    constexpr int CH = PI::CH;
+    static_assert(CH % 4 == 0 && 64 % CPR == 0, "bad chunking");
+    static_assert(L::D0 % RB == 0 && L::D % RB == 0, "row blocks must not straddle estimator terms");
+    const int lane = tid & 63, wv = tid / 64;
+    for (int e = tid; e < NQ4 * L::D; e += NT) {
+        const int qq = e / L::D, c = e % L::D, gq = q0 + qq;
+        float a = pr.qv, b = pr.qg;
+        if (e != tid) {
+            const float *qrow = q + ((size_t)bank * G + gq) * L::D;
+            a = gq < G ? qrow[c] : 0.0f;
+            b = gq < G ? qrow[chan ? chan[c] : c] : 0.0f;
+        }
+        ps.qv[c][qq] = a;
+        ps.qg[c][qq] = b;
+    }
+    prep_barrier<LDS_ONLY>();
+    // GEMV items; parts of a row sit in adjacent lanes, rows of a wave form one row block;
+    // both are reduced with shuffles in a fixed order.
+    for (int it = tid; it < NR * RT * CPR; it += NT) {
+        const PI pi(it, rot, proj);
+        const int part = pi.part, r = pi.r, qb = pi.qb;
+        const float(*src)[NQ4] = pi.rotated ? ps.qg + pi.off : ps.qv;  // operand columns of this row
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         {
             f32x4 m[CH / 4];
+            const int k = (it - tid) / NT;
+            if (k < PrepRegs<L, RT, NT>::PRE) {
 #pragma unroll
-            for (int i = 0; i < CH / 4; ++i) {
-                const int k = 4 * (i * CPR + part);
-                m[i] = k < K ? *reinterpret_cast<const f32x4 *>(row + k) : f32x4{0, 0, 0, 0};
+                for (int kk = 0; kk < PrepRegs<L, RT, NT>::PRE; ++kk)
+                    if (kk == k)
+#pragma unroll
+                        for (int i = 0; i < CH / 4; ++i) m[i] = pr.m[kk][i];
+            } else {
+                pi.load(m);
             }
 #pragma unroll
             for (int i = 0; i < CH / 4; ++i) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int k = min(4 * (i * CPR + part) + e, K - 1);  // past K the loaded value is 0
+                    const int k = min(4 * (i * CPR + part) + e, pi.K - 1);  // past K the loaded value is 0
                     const f32x4 qc = *reinterpret_cast<const f32x4 *>(&src[k][qb]);
 #pragma unroll
                     for (int qq = 0; qq < 4; ++qq) acc[qq] = fmaf(m[i][e], qc[qq], acc[qq]);
@@ -143,9 +242,10 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
                 ps.psum[r / RB][qb + qq] = sm[qq];
             }
     }
-    __syncthreads();
+    prep_barrier<LDS_ONLY>();
+    after_gemv();
     // per (query, term): exponent F from the max |weight|, additive constant from the sum
-    for (int it = tid; it < NQ4 * L::NCLS; it += NT) {
+    for (int it = tid; tail_worker && it < NQ4 * L::NCLS; it += NT_TAIL) {
         const int qq = it / L::NCLS, c = it % L::NCLS, gq = q0 + qq;
         const int r0 = c < L::NG ? (c ? L::D0 : 0) : L::D;
         const int r1 = c < L::NG ? (c ? L::D : L::D0) : NR;
@@ -154,11 +254,15 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
             mx = fmax(mx, (double)ps.pmax[bk][qq]);
             sm += ps.psum[bk][qq];
         }
+        // (kernel-argument arrays are indexed with constants only: a runtime index would
+        // read them through vector memory)
         double wmax;
         if (c < L::NG) {
             double cm = 0.0;
             const int nsub = walsh_planes(c ? L::B1 : L::B0);
-            for (int s2 = 0; s2 < nsub; ++s2) cm = fmax(cm, fabs(pa.walsh[c][s2]));
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                if (s2 < nsub) cm = fmax(cm, fabs(c ? pa.walsh[1][s2] : pa.walsh[0][s2]));
             wmax = mx * cm;
         } else {
             wmax = 2.0 * mx;
@@ -169,12 +273,12 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
         ps.F[qq][c] = F;
         double *o = const_out + ((size_t)qq * L::NCLS + c) * 2;
         o[0] = ldexp(1.0, -F);
-        o[1] = gq < G ? (c < L::NG ? -pa.cmax[c] * sm : -sm) : 0.0;
+        o[1] = gq < G ? (c < L::NG ? -(c ? pa.cmax[1] : pa.cmax[0]) * sm : -sm) : 0.0;
     }
-    __syncthreads();
+    prep_barrier<LDS_ONLY>();
     // fragments: RT waves per fragment (wave-uniform fragment id); item (gl, query, dword v)
     // -> 4 K positions x 4 limbs (one dword in each of four lanes)
-    for (int fw = wv; fw < L::NF * RT; fw += NT / 64) {
+    for (int fw = wv; tail_worker && fw < L::NF * RT; fw += NT_TAIL / 64) {
         const int fr = fw / RT, it = (fw % RT) * 64 + lane;
         const int v = it & 3, qq = (it >> 2) % NQ4, gl = (it >> 2) / NQ4;
         static_for<L::NF>([&](auto fcst) {
@@ -192,7 +296,12 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
             const int t = 4 * fh + v;
             const double scale = ldexp(1.0, ps.F[qq][fc] - t);  // 2^(F - t)
             const float *src = fc < L::NG ? &ps.w[qq][(fc ? L::D0 : 0) + 32 * wk] : &ps.w[qq][L::D + 32 * wk];
-            const double mul = fc < L::NG ? pa.walsh[fc][sub] : 2.0;
+            constexpr int fg = fc < L::NG ? fc : 0;
+            const double mul = fc < L::NG ? (sub == 0   ? pa.walsh[fg][0]
+                                             : sub == 1 ? pa.walsh[fg][1]
+                                             : sub == 2 ? pa.walsh[fg][2]
+                                                        : pa.walsh[fg][3])
+                                          : 2.0;
             uint32_t U[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -212,6 +321,16 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
             }
         });
     }
+}
+
+template <class L, int RT, int NT>
+__device__ __forceinline__ void prep_operands(int tid, const float *__restrict__ q, long bank, int G, int q0,
+                                              const float *__restrict__ rot, const float *__restrict__ proj,
+                                              const int *__restrict__ chan, const PrepArgs &pa,
+                                              PrepScratch<L, RT> &ps, int8_t *frag_out, double *const_out) {
+    PrepRegs<L, RT, NT> pr;
+    prep_load<L, RT, NT>(pr, tid, q, bank, G, q0, rot, proj, chan);
+    prep_finish<L, RT, NT>(pr, tid, q, bank, G, q0, rot, proj, chan, pa, ps, frag_out, const_out);
 }
 
 // Standalone query preparation: one 1024-thread work-group per (bank, row tile of 4 queries).
@@ -475,11 +594,15 @@ __global__ __launch_bounds__(fused_waves<RT>() * 64) void score_fused_kernel(
     TileStream<L, RT, TB> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
                              rnorms + (size_t)bank * n_pad, scores + (size_t)bank * G * n, n, G, t0, t1};
     ts.init_lane();
-    // the first two batches are requested before the prologue, which then overlaps their latency
+    // the prologue's own reads go first, then the first two batches of tiles, whose latency
+    // the rest of the prologue overlaps (loads complete in issue order)
+    PrepRegs<L, RT, WAVES * 64> pr;
+    prep_load<L, RT, WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan);
+    asm volatile("" ::: "memory");
     TileBatch<L, TB> A, B;
     ts.prefetch(A, B);
-    prep_operands<L, RT, WAVES * 64>(tid, q, bank, G, 0, rot, proj, chan, pa, lds.ps, &lds.frags[0][0][0][0],
-                                     &lds.consts[0][0][0]);
+    prep_finish<L, RT, WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, lds.ps, &lds.frags[0][0][0][0],
+                                   &lds.consts[0][0][0]);
     __syncthreads();
     if (t0 >= t1) return;
     i8x16 wf[RT][L::NF];
@@ -496,6 +619,249 @@ __global__ __launch_bounds__(fused_waves<RT>() * 64) void score_fused_kernel(
             ck[rt][c] = lds.consts[4 * rt + gl][c][1];
         }
     ts.run(A, B, wf, cs, ck, sc);
+}
+
+// ------------------------------------------------------------------------------------------
+// Ring-staged fused scorer for up to 4 queries per bank. Key tiles move from HBM straight
+// into LDS (global_load_lds_dwordx4), S tiles ahead of the compute in every wave, so the
+// loads in flight hold no VGPRs and the first S tiles of every wave stream in while the
+// work-group builds its query operands.
+//
+// A tile slot holds the tile's W bit rows (64 B each: one word of 16 keys), its NG norm rows
+// and its residual-norm row, in that order. The waits count only the direct loads issued
+// after the awaited tile; loads complete in issue order, so such a wait is exact for the
+// tile whatever the score stores pending beside them (it may also wait on those stores,
+// which is why each score is stored two tiles late).
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in [15:14])
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int waitcnt_lgkm0() { return 15 | (7 << 4) | (3 << 14); }
+
+template <class L>
+struct RingTile {
+    static constexpr int ROWS = L::W + L::NG + 1;
+    static constexpr int WORDS = ROWS * 16;
+    static constexpr int BIT_LOADS = (L::W + 15) / 16;  // 1 KiB direct loads for the bit rows
+    static constexpr int LOADS = BIT_LOADS + 1;         // and one for the norm rows
+    static_assert(L::NG + 1 <= 16, "norm rows exceed one load");
+};
+
+constexpr int RING_WAVES = 16;
+
+template <class L>
+constexpr int ring_slots() {
+    // the ring and the prologue's scratch within 160 KiB of LDS; at most 8 tiles ahead
+    constexpr int budget = 160 * 1024 - (int)sizeof(FusedLds<L, 1>);
+    constexpr int s = budget / (RING_WAVES * RingTile<L>::WORDS * 4);
+    return (s > 8 ? 8 : s) & ~1;  // even: the steady state fills the ring by halves
+}
+
+// Issues the direct loads of one tile into a slot (every lane of the wave calls it):
+// `tile_bits` is the tile's bit block, `nr_src` this lane's 16 bytes of the tile's norm
+// rows (lanes below 4*NG: norms; the next four lanes: residual norms; see NormLane).
+template <class L>
+__device__ __forceinline__ void ring_fetch(const char *tile_bits, const float *nr_src, lds_u32 *slot, int lane) {
+    static_for<RingTile<L>::BIT_LOADS>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int rows = L::W - 16 * i < 16 ? L::W - 16 * i : 16;
+        if (rows == 16 || lane < 4 * rows)
+            __builtin_amdgcn_global_load_lds(tile_bits + 1024 * i + 16 * lane, (lds_void *)(slot + 256 * i), 16, 0,
+                                             0);
+    });
+    if (lane < 4 * (L::NG + 1)) __builtin_amdgcn_global_load_lds(nr_src, (lds_void *)(slot + 16 * L::W), 16, 0, 0);
+}
+
+// A lane's share of the norm rows: its source for tile 0 and its stride per tile.
+template <class L>
+struct NormLane {
+    const float *base;
+    int stride;  // floats per tile
+    __device__ __forceinline__ NormLane(const float *nb, const float *rb, int lane) {
+        const bool is_nu = lane < 4 * L::NG;
+        base = is_nu ? nb + 4 * lane : rb + 4 * (lane - 4 * L::NG);
+        stride = is_nu ? 16 * L::NG : 16;
+    }
+    __device__ __forceinline__ const float *at(int tile) const { return base + (size_t)tile * stride; }
+};
+
+template <class L>
+__device__ __forceinline__ const char *tile_bits(const uint32_t *bb, int tile) {
+    return reinterpret_cast<const char *>(bb + (size_t)tile * (L::W * 16));
+}
+
+// Waits until at most `ahead` tiles' direct loads (and nothing older) are outstanding.
+template <class L, int S>
+__device__ __forceinline__ void ring_wait(int ahead) {
+    static_for<S>([&](auto ac) {
+        constexpr int a = decltype(ac)::value;
+        if (ahead == a) __builtin_amdgcn_s_waitcnt(waitcnt_vm(a * RingTile<L>::LOADS));
+    });
+}
+
+template <class L, int S>
+__global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
+    const uint32_t *__restrict__ bits, const float *__restrict__ norms, const float *__restrict__ rnorms,
+    const float *__restrict__ q, const float *__restrict__ rot, const float *__restrict__ proj,
+    const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks, long n, int n_tiles, int G,
+    int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
+    using RTL = RingTile<L>;
+    __shared__ FusedLds<L, 1> lds;
+    __shared__ __attribute__((aligned(16))) uint32_t ring_mem[RING_WAVES][S][RTL::WORDS];
+    const long bank = blockIdx.x / wgs_per_bank;
+    const int part = blockIdx.x % wgs_per_bank;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, gl = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int w0 = part * tiles_per_wg, w1 = min(w0 + tiles_per_wg, n_tiles);
+    const int per = (w1 - w0 + RING_WAVES - 1) / RING_WAVES;
+    const int t0 = min(w0 + wv * per, w1), t1 = min(t0 + per, w1);
+    const int nt = t1 - t0;
+    const long n_pad = (long)n_tiles * 16;
+    const uint32_t *bb = bits + (size_t)bank * n_tiles * L::W * 16;
+    const float *nb = norms + (size_t)bank * n_pad * L::NG;
+    const float *rb = rnorms + (size_t)bank * n_pad;
+    float *ob = scores + (size_t)bank * G * n;
+    lds_u32 *ring = (lds_u32 *)&ring_mem[wv][0][0];
+
+    // Prologue. All waves load and stage the query and run the GEMV from registers (one
+    // matrix chunk per thread). After the GEMV barrier the upper half of the waves issues
+    // the ring fill of every wave (its partner's first, then its own) while the lower half
+    // finishes the operands: those waves have no direct-to-LDS loads pending, so none of
+    // their LDS accesses waits on the fill. Before the last barrier each filler waits for
+    // its partner's fill (issued first, so its own stays in flight).
+    constexpr int HALF = RING_WAVES / 2;
+    const bool filler = wv >= HALF;
+    const int tlast = max(t1 - 1, 0);
+    PrepRegs<L, 1, RING_WAVES * 64> pr;
+    prep_load<L, 1, RING_WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan);
+    auto fill = [&]() {
+        if (!filler) return;
+        const int pv = wv - HALF;  // partner wave: same split of the work-group's tiles
+        const int pt0 = min(w0 + pv * per, w1), pt1 = min(pt0 + per, w1), plast = max(pt1 - 1, 0);
+        lds_u32 *pring = (lds_u32 *)&ring_mem[pv][0][0];
+        const NormLane<L> nl(nb, rb, lane);
+        // slots past a short run reload its last tile, so the fill has no branches
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int t = min(pt0 + i, plast);
+            ring_fetch<L>(tile_bits<L>(bb, t), nl.at(t), pring + i * RTL::WORDS, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int t = min(t0 + i, tlast);
+            ring_fetch<L>(tile_bits<L>(bb, t), nl.at(t), ring + i * RTL::WORDS, lane);
+        }
+    };
+    prep_finish<L, 1, RING_WAVES * 64, true, HALF * 64>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, lds.ps,
+                                                        &lds.frags[0][0][0][0], &lds.consts[0][0][0], fill, !filler);
+    if (filler) __builtin_amdgcn_s_waitcnt(waitcnt_vm(S * RTL::LOADS));
+    lds_barrier();
+    if (nt <= 0) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        return;
+    }
+    i8x16 wf[1][L::NF];
+#pragma unroll
+    for (int f = 0; f < L::NF; ++f) wf[0][f] = *reinterpret_cast<const i8x16 *>(&lds.frags[0][f][lane][0]);
+    // per-term constants with the term's scale folded in: est = sum_c s_c (S_c cs_c + ck_c),
+    // s_c = nu_g for the code terms of group g and rho for the sketch term
+    double cs[L::NCLS], ck[L::NCLS];
+    static_for<L::NCLS>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int g = c < L::NG ? c : 0;
+        const double f = c < L::NG ? sc.inv_sqrt_d[g] : sc.qjl;
+        cs[c] = lds.consts[gl][c][0] * f;
+        ck[c] = lds.consts[gl][c][1] * f;
+    });
+    // per-lane word offsets inside a slot (lane group gl takes word 4s+gl of key j)
+    int woff[L::NSQ];
+    bool wlive[L::NSQ];
+#pragma unroll
+    for (int s = 0; s < L::NSQ; ++s) {
+        wlive[s] = 4 * s + gl < L::W;
+        woff[s] = (wlive[s] ? 4 * s + gl : 0) * 16 + j;
+    }
+    const NormLane<L> nl(nb, rb, lane);
+
+    auto read_slot = [&](const volatile lds_u32 *slot, uint32_t(&sw)[L::NSQ], float(&nu)[L::NG], float &rho) {
+#pragma unroll
+        for (int s = 0; s < L::NSQ; ++s) sw[s] = slot[woff[s]];
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) nu[g] = __uint_as_float(slot[16 * L::W + j * L::NG + g]);
+        rho = __uint_as_float(slot[16 * (L::W + L::NG) + j]);
+        // the slot's reads are done before the next tile's loads overwrite it
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+#pragma unroll
+        for (int s = 0; s < L::NSQ; ++s)
+            if (!wlive[s]) sw[s] = 0u;
+    };
+    auto tile_est = [&](const uint32_t(&sw)[L::NSQ], const float(&nu)[L::NG], float rho) -> float {
+        i32x4 acc[1][L::NCLS];
+        score_tile<L, 1>(sw, wf, acc);
+        double est = 0.0;
+        static_for<L::NCLS>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            constexpr int g = c < L::NG ? c : 0;
+            const double s = c < L::NG ? (double)nu[g] : (double)rho;
+            est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[0][c]), cs[c], ck[c]), est);
+        });
+        return (float)est;
+    };
+
+    // Steady state, for four live queries: groups of U = S/2 tiles that fill one half of the
+    // ring, so tile i sits in slot (i / U odd ? U : 0) + k for its position k in the group;
+    // every refill stays inside the run and every key is below n. Waits, store offsets and
+    // slot offsets inside a half are then constants; the scores of a group are stored
+    // during the next one.
+    constexpr int U = S / 2;
+    static_assert(S % 2 == 0, "the ring is filled by halves");
+    int i = 0;
+    const int full = (int)(n >> 4);  // tiles whose 16 keys are all below n
+    const int loff = gl * (int)n + j;  // lane offset into the bank's score rows
+    if (G == 4 && 2 * S <= nt && t0 + U <= full) {
+        float pend[U];
+        auto group = [&](auto store_prev) {
+            constexpr bool SP = decltype(store_prev)::value;
+            float *prev_out = ob + (size_t)(t0 + i - U) * 16;
+            lds_u32 *half = ring + ((i / U) & 1) * (U * RTL::WORDS);
+            static_for<U>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 1) * RTL::LOADS));
+                uint32_t sw[L::NSQ];
+                float nu[L::NG], rho;
+                read_slot(half + k * RTL::WORDS, sw, nu, rho);
+                if constexpr (SP) prev_out[loff + 16 * k] = pend[k];
+                const int tn = t0 + i + S + k;
+                ring_fetch<L>(tile_bits<L>(bb, tn), nl.at(tn), half + k * RTL::WORDS, lane);
+                pend[k] = tile_est(sw, nu, rho);
+            });
+            i += U;
+        };
+        group(std::false_type{});
+        while (i + S + U <= nt && t0 + i + U <= full) group(std::true_type{});
+        float *last_out = ob + (size_t)(t0 + i - U) * 16;
+        static_for<U>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            last_out[loff + 16 * k] = pend[k];
+        });
+    }
+    // the rest one tile at a time: waits by the loads actually issued after the tile,
+    // refills while inside the run, stores checked against G and n
+    const bool qlive = gl < G;
+    for (; i < nt; ++i) {
+        ring_wait<L, S>(min(S - 1, nt - 1 - i));
+        uint32_t sw[L::NSQ];
+        float nu[L::NG], rho;
+        read_slot(ring + (i % S) * RTL::WORDS, sw, nu, rho);
+        if (i + S < nt) {
+            const int tn = t0 + i + S;
+            ring_fetch<L>(tile_bits<L>(bb, tn), nl.at(tn), ring + (i % S) * RTL::WORDS, lane);
+        }
+        const float est = tile_est(sw, nu, rho);
+        if (qlive && (long)(t0 + i) * 16 + j < n) ob[(size_t)(t0 + i) * 16 + loff] = est;
+    }
 }
 
 }  // namespace tq
