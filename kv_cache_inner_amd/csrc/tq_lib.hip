@@ -10,6 +10,7 @@
 #include "../../include/tq.h"
 #include "tq_encode.h"
 #include "tq_score.h"
+#include "tq_topk.h"
 #include "tq_measure.h"
 
 using namespace tq;
@@ -197,6 +198,35 @@ static PrepPlan prep_plan(int NF, int NCLS, int64_t banks, int32_t G) {
 
 static size_t encode_ws(const tq_params *p) { return align256((size_t)p->m * p->d * 4); }
 
+// LDS-operand scorer / top-k: row tiles per work-group, query blocks, key chunks
+struct LdsPlan {
+    int qblocks, kchunks, chunk_tiles;
+    int64_t grid;
+};
+template <class L>
+static LdsPlan lds_plan(int64_t banks, int64_t n, int Gpad) {
+    LdsPlan pl;
+    constexpr int RQ = lds_rows<L>();
+    pl.qblocks = (Gpad / 4 + RQ - 1) / RQ;
+    const int64_t n_tiles = (n + 15) / 16;
+    // about 1024 work-groups (one per compute unit at a time, four rounds), each wave
+    // keeping at least a few tiles
+    int64_t kc = (1024 + banks * pl.qblocks - 1) / (banks * pl.qblocks);
+    int64_t max_kc = n_tiles / (4 * LDS_WAVES);
+    if (max_kc < 1) max_kc = 1;
+    if (kc > max_kc) kc = max_kc;
+    if (kc < 1) kc = 1;
+    pl.chunk_tiles = (int)((n_tiles + kc - 1) / kc);
+    pl.kchunks = (int)((n_tiles + pl.chunk_tiles - 1) / pl.chunk_tiles);
+    pl.grid = banks * pl.kchunks * pl.qblocks;
+    return pl;
+}
+
+// top-k partial lists: [banks][G][kchunks * LDS_WAVES][k] values, then indices
+static size_t topk_part_bytes(int64_t banks, int32_t G, int kchunks, int32_t k) {
+    return align256((size_t)banks * G * kchunks * LDS_WAVES * k * 4);
+}
+
 extern "C" size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k) {
     if (check_params(p) || banks < 0 || n < 0) return 0;
     if (op == TQ_OP_ENCODE) return encode_ws(p);
@@ -211,7 +241,14 @@ extern "C" size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, 
     if (op == TQ_OP_SCORE) return out;
     if (op == TQ_OP_TOPK) {
         if (k < 1 || k > 64) return 0;
-        return out + align256(topk_partial_bytes(banks, G, n, k));
+        size_t part = 0;
+        with_layout(p, [&](auto l) {
+            using L = decltype(l);
+            const LdsPlan lp = lds_plan<L>(banks, n, 4 * ((G + 3) / 4));
+            part = 2 * topk_part_bytes(banks, G, lp.kchunks, k);
+            return TQ_OK;
+        });
+        return out + part;
     }
     return 0;
 }
@@ -419,6 +456,25 @@ static int launch_ring(const tq_params *p, const tq_bank *in, int64_t banks, int
     }
 }
 
+// Scorer / top-k with the prepared operands staged in LDS (any G, any layout whose
+// operands of one row tile fit). TOPK: partial lists into part_v / part_i.
+template <class L, bool TOPK>
+static int launch_lds(const tq_bank *in, int64_t banks, int64_t n, int32_t G, const PrepPlan &pp, const void *ws,
+                      float *scores, int32_t k, float *part_v, int *part_i, const ScoreScale &sc, hipStream_t st) {
+    if constexpr (!lds_fits<L>()) {
+        return TQ_ERR_UNSUPPORTED;
+    } else {
+        const LdsPlan lp = lds_plan<L>(banks, n, pp.Gpad);
+        if (lp.grid > INT32_MAX || (int64_t)G * n > ((int64_t)1 << 62)) return TQ_ERR_UNSUPPORTED;
+        const int8_t *frags = (const int8_t *)ws;
+        const double *consts = (const double *)((const char *)ws + pp.const_off);
+        hipLaunchKernelGGL((score_lds_kernel<L, lds_rows<L>(), TOPK>), dim3((unsigned)lp.grid), dim3(LDS_WAVES * 64),
+                           0, st, in->bits, in->norms, in->rnorms, frags, consts, (long)n, (int)((n + 15) / 16), (int)G,
+                           pp.Gpad, lp.qblocks, lp.kchunks, lp.chunk_tiles, sc, scores, (int)k, part_v, part_i);
+        return launch_status();
+    }
+}
+
 extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
                                  const void *workspace, float *scores, void *stream) {
     int rc = check_params(p);
@@ -427,18 +483,22 @@ extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t 
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
-    if (G > 16) return TQ_ERR_UNSUPPORTED;
     const ScoreScale sc = score_scale(p);
     return with_layout(p, [&](auto l) {
         using L = decltype(l);
         const PrepPlan pl = prep_plan(L::NF, L::NCLS, banks, G);
         hipStream_t st = (hipStream_t)stream;
+        int r = TQ_ERR_UNSUPPORTED;
         switch (pl.Gpad / 4) {
-            case 1: return launch_score<L, 1>(in, banks, n, G, pl, workspace, scores, sc, st);
-            case 2: return launch_score<L, 2>(in, banks, n, G, pl, workspace, scores, sc, st);
-            case 3: return launch_score<L, 3>(in, banks, n, G, pl, workspace, scores, sc, st);
-            default: return launch_score<L, 4>(in, banks, n, G, pl, workspace, scores, sc, st);
+            case 1: r = launch_score<L, 1>(in, banks, n, G, pl, workspace, scores, sc, st); break;
+            case 2: r = launch_score<L, 2>(in, banks, n, G, pl, workspace, scores, sc, st); break;
+            case 3: r = launch_score<L, 3>(in, banks, n, G, pl, workspace, scores, sc, st); break;
+            case 4: r = launch_score<L, 4>(in, banks, n, G, pl, workspace, scores, sc, st); break;
+            default: break;
         }
+        if (r != TQ_ERR_UNSUPPORTED) return r;
+        // many queries, or operands too large for registers: operands in LDS
+        return launch_lds<L, false>(in, banks, n, G, pl, workspace, scores, 0, nullptr, nullptr, sc, st);
     });
 }
 
@@ -449,9 +509,8 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
     if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q) return TQ_ERR_ARG;
-    if (G > 16) return TQ_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
-    rc = with_layout(p, [&](auto l) {
+    rc = G > 16 ? (int)TQ_ERR_UNSUPPORTED : with_layout(p, [&](auto l) {
         using L = decltype(l);
         switch ((G + 3) / 4) {
             case 1: {
@@ -465,7 +524,8 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
         }
     });
     if (rc != TQ_ERR_UNSUPPORTED) return rc;
-    // layouts too large for the fused prologue: prepare into the workspace, then score
+    // many queries, or layouts too large for the fused prologue: prepare into the
+    // workspace, then score
     if ((rc = tq_prepare_queries(p, q, banks, G, workspace, ws_bytes, stream))) return rc;
     return tq_score_prepared(p, in, banks, n, G, workspace, scores, stream);
 }
@@ -477,10 +537,30 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
     if (banks < 0 || n < 0 || G < 1 || k < 1 || k > 64 || k > n) return TQ_ERR_ARG;
     if (banks == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx) return TQ_ERR_ARG;
-    (void)workspace;
-    (void)ws_bytes;
-    (void)stream;
-    return TQ_ERR_UNSUPPORTED;
+    if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    if (ws_bytes < tq_workspace_bytes(TQ_OP_TOPK, p, banks, n, G, k)) return TQ_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const ScoreScale sc = score_scale(p);
+    return with_layout(p, [&](auto l) {
+        using L = decltype(l);
+        if constexpr (!lds_fits<L>()) {
+            return (int)TQ_ERR_UNSUPPORTED;
+        } else {
+            const PrepPlan pp = prep_plan(L::NF, L::NCLS, banks, G);
+            const LdsPlan lp = lds_plan<L>(banks, n, pp.Gpad);
+            if (banks * G > INT32_MAX / 2) return (int)TQ_ERR_UNSUPPORTED;
+            const size_t pb = topk_part_bytes(banks, G, lp.kchunks, k);
+            float *part_v = (float *)((char *)workspace + pp.total);
+            int *part_i = (int *)((char *)workspace + pp.total + pb);
+            int r = tq_prepare_queries(p, q, banks, G, workspace, ws_bytes, stream);
+            if (r) return r;
+            if ((r = launch_lds<L, true>(in, banks, n, G, pp, workspace, nullptr, k, part_v, part_i, sc, st))) return r;
+            const int64_t queries = banks * G;
+            hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((queries + 3) / 4)), dim3(256), 0, st, part_v, part_i,
+                               (long)queries, lp.kchunks * LDS_WAVES, (int)k, vals, (int *)idx);
+            return launch_status();
+        }
+    });
 }
 
 extern "C" int tq_fp32_logits(const float *keys, int64_t banks, int64_t n, int32_t d, const float *q, int32_t G,

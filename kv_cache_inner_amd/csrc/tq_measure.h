@@ -67,11 +67,4 @@ inline int launch_copy(const void *src, void *dst, size_t bytes, hipStream_t st)
     return hipGetLastError() != hipSuccess;
 }
 
-// Top-k partial results: per (bank, query, key chunk) k candidates (value, index).
-inline size_t topk_partial_bytes(int64_t banks, int32_t G, int64_t n, int32_t k) {
-    (void)n;
-    const int64_t chunks = 1024;
-    return (size_t)banks * G * chunks * k * 8;
-}
-
 }  // namespace tq

@@ -1,0 +1,240 @@
+// Scorer with the query operands in LDS, and the fused per-query top-k.
+//
+// Vector search (tambur.pub article on TurboQuant, vector-search paragraph: the packed
+// database is searched directly by estimated inner products; turboquant-pytorch write-up,
+// usage example: inner_product(query, compressed)) needs many queries per bank and large
+// key dimensions, whose MFMA operands do not fit in registers. Here a work-group stages
+// the prepared operands (tq_prepare_queries) of RQ row tiles of one bank in LDS, and each
+// of its waves streams a contiguous run of that bank's 16-key tiles, reading every operand
+// fragment from LDS as it is used. The estimates are then either stored (scores) or kept
+// as a running per-query top-k that never leaves the chip until the end.
+//
+// Top-k: the k best (value, index) pairs of a query live across the lanes of a wave, entry
+// i in lane i, best first (larger value; equal values by lower index). A tile's estimates
+// that beat the k-th entry are inserted one at a time by a lane-parallel shift. Each wave
+// writes its k entries per query as a partial list; a merge kernel reduces the partial
+// lists of a query to the final top-k.
+#pragma once
+#include "tq_score.h"
+
+namespace tq {
+
+constexpr int LDS_WAVES = 16;
+
+// row tiles of operands a work-group holds in LDS (fragments and constants in ~150 KiB)
+template <class L>
+constexpr int lds_rows() {
+    constexpr int per = L::NF * 1024 + 4 * L::NCLS * 16;
+    constexpr int r = (150 * 1024) / per;
+    return r > 4 ? 4 : (r < 1 ? 1 : r);
+}
+
+template <class L>
+constexpr bool lds_fits() {
+    return L::NF * 1024 + 4 * L::NCLS * 16 <= 150 * 1024;
+}
+
+// Entry i of a per-query list sits in lane i. `better` orders candidates: larger value
+// first, equal values by lower index.
+__device__ __forceinline__ bool topk_better(float v, int i, float lv, int li) { return v > lv || (v == lv && i < li); }
+
+// Inserts (v, id) into the wave-distributed sorted list (lv, li) (entries past k-1 are
+// dropped off the end by the shift; lanes >= k hold entries that are never read back).
+__device__ __forceinline__ void topk_insert(float &lv, int &li, float v, int id, int lane) {
+    const bool b = topk_better(v, id, lv, li);
+    const float pv = __shfl_up(lv, 1, 64);
+    const int pi = __shfl_up(li, 1, 64);
+    const bool pb = __shfl_up(b ? 1 : 0, 1, 64) != 0 && lane > 0;
+    if (b) {
+        lv = pb ? pv : v;
+        li = pb ? pi : id;
+    }
+}
+
+// Offers the 16 estimates of lane group g (key index key, valid flag ok) to query list
+// (lv, li): those that beat the current k-th entry are inserted in lane order.
+__device__ __forceinline__ void topk_offer(float &lv, int &li, float est, int key, bool ok, int g, int gl, int k,
+                                           int lane) {
+    const float tv = __shfl(lv, k - 1, 64);
+    const int ti = __shfl(li, k - 1, 64);
+    uint64_t m = __ballot(ok && gl == g && topk_better(est, key, tv, ti));
+    while (m) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1;
+        const float v = __shfl(est, src, 64);
+        const int id = __shfl(key, src, 64);
+        topk_insert(lv, li, v, id, lane);
+    }
+}
+
+template <class L, int RQ, bool TOPK>
+__global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
+    const uint32_t *__restrict__ bits, const float *__restrict__ norms, const float *__restrict__ rnorms,
+    const int8_t *__restrict__ frags, const double *__restrict__ consts, long n, int n_tiles, int G, int Gpad,
+    int qblocks, int kchunks, int chunk_tiles, ScoreScale sc, float *__restrict__ scores, int k,
+    float *__restrict__ part_v, int *__restrict__ part_i) {
+    __shared__ __attribute__((aligned(16))) int8_t fa[RQ][L::NF][64][16];
+    __shared__ double cst[4 * RQ][L::NCLS][2];
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, gl = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // block -> (bank, key chunk, query block), query block fastest: the work-groups that
+    // read the same key chunk run side by side
+    int blk = blockIdx.x;
+    const int qb = blk % qblocks;
+    blk /= qblocks;
+    const int kc = blk % kchunks;
+    const long bank = blk / kchunks;
+    const int NRT = Gpad / 4, rt0 = qb * RQ;
+
+    // stage this block's operands (row tiles past the bank's last are zero)
+    const int8_t *fsrc = frags + ((size_t)bank * NRT + rt0) * L::NF * 1024;
+    for (int e = tid; e < RQ * L::NF * 64; e += LDS_WAVES * 64) {
+        const int rt = e / (L::NF * 64);
+        const u32x4 v = rt0 + rt < NRT ? *reinterpret_cast<const u32x4 *>(fsrc + (size_t)e * 16) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(&fa[0][0][0][0] + (size_t)e * 16) = v;
+    }
+    for (int e = tid; e < 4 * RQ * L::NCLS * 2; e += LDS_WAVES * 64) {
+        const int qq = e / (L::NCLS * 2), r = e % (L::NCLS * 2);
+        const int gq = 4 * rt0 + qq;
+        (&cst[0][0][0])[e] = gq < Gpad ? consts[((size_t)bank * Gpad + gq) * L::NCLS * 2 + r] : 0.0;
+    }
+    __syncthreads();
+    // per (row tile, term): constants of this lane's query with the term's scale folded in
+    double cs[RQ][L::NCLS], ck[RQ][L::NCLS];
+#pragma unroll
+    for (int rt = 0; rt < RQ; ++rt)
+        static_for<L::NCLS>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            constexpr int g = c < L::NG ? c : 0;
+            const double f = c < L::NG ? sc.inv_sqrt_d[g] : sc.qjl;
+            cs[rt][c] = cst[4 * rt + gl][c][0] * f;
+            ck[rt][c] = cst[4 * rt + gl][c][1] * f;
+        });
+
+    // this wave's contiguous run of the chunk's tiles
+    const int c0 = kc * chunk_tiles, c1 = min(c0 + chunk_tiles, n_tiles);
+    const int per = (c1 - c0 + LDS_WAVES - 1) / LDS_WAVES;
+    const int t0 = min(c0 + wv * per, c1), t1 = min(t0 + per, c1);
+    const long n_pad = (long)n_tiles * 16;
+    TileStream<L, 1, 1> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
+                           rnorms + (size_t)bank * n_pad, nullptr, n, G, t0, t1};
+    ts.init_lane();
+    float *ob = TOPK ? nullptr : scores + (size_t)bank * G * n;
+
+    // per-query top-k lists (4 queries per row tile), entry i in lane i
+    float lv[TOPK ? RQ * 4 : 1];
+    int li[TOPK ? RQ * 4 : 1];
+#pragma unroll
+    for (int e = 0; e < (TOPK ? RQ * 4 : 1); ++e) {
+        lv[e] = -INFINITY;
+        li[e] = INT32_MAX;
+    }
+
+    TileBatch<L, 1> A, B;
+    if (t0 < t1) ts.load(A, t0);
+    for (int t = t0; t < t1; ++t) {
+        if (t + 1 < t1) ts.load(B, t + 1);
+        i32x4 acc[RQ][L::NCLS];
+#pragma unroll
+        for (int rt = 0; rt < RQ; ++rt)
+#pragma unroll
+            for (int c = 0; c < L::NCLS; ++c) acc[rt][c] = i32x4{0, 0, 0, 0};
+        static_for<L::NQ>([&](auto qc) {
+            constexpr int qd = decltype(qc)::value;
+            constexpr int nx = L::quad_nx(qd);
+            uint32_t der = A.sw[0][L::quad_sq(qd, 0)];
+            if constexpr (nx > 1) der ^= A.sw[0][L::quad_sq(qd, 1)];
+            if constexpr (nx > 2) der ^= A.sw[0][L::quad_sq(qd, 2)];
+            static_for<2>([&](auto hc) {
+                constexpr int h = decltype(hc)::value;
+                const i8x16 b = expand_half<h>(der);
+                static_for<L::NCLS>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    if constexpr (L::quad_has(qd, c)) {
+                        constexpr int f = L::frag_index(qd, h, c);
+#pragma unroll
+                        for (int rt = 0; rt < RQ; ++rt) {
+                            const i8x16 a = *reinterpret_cast<const i8x16 *>(&fa[rt][f][lane][0]);
+                            acc[rt][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rt][c], 0, 0, 0);
+                        }
+                    }
+                });
+            });
+            // the fragment reads of later quads stay below this point (all of them live at
+            // once would exceed the register budget)
+            asm volatile("" ::: "memory");
+        });
+        const long key = (long)t * 16 + j;
+        const bool key_live = key < n;
+#pragma unroll
+        for (int rt = 0; rt < RQ; ++rt) {
+            double est = 0.0;
+            static_for<L::NCLS>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                constexpr int g = c < L::NG ? c : 0;
+                const double s = c < L::NG ? (double)A.nu[0][g] : (double)A.rho[0];
+                est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[rt][c]), cs[rt][c], ck[rt][c]), est);
+            });
+            const float e = (float)est;
+            const int gq = 4 * (rt0 + rt) + gl;
+            if constexpr (TOPK) {
+                // queries past G never enter a list (their lists are not written back)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    topk_offer(lv[4 * rt + g], li[4 * rt + g], e, (int)key, key_live && gq < G, g, gl, k, lane);
+            } else {
+                if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
+            }
+        }
+        A = B;
+    }
+    if constexpr (TOPK) {
+        // partial lists: [bank][query][chunk * LDS_WAVES + wave][k]
+        const int slots = kchunks * LDS_WAVES, slot = kc * LDS_WAVES + wv;
+#pragma unroll
+        for (int rt = 0; rt < RQ; ++rt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int gq = 4 * (rt0 + rt) + g;
+                if (gq < G && lane < k) {
+                    const size_t o = (((size_t)bank * G + gq) * slots + slot) * k + lane;
+                    part_v[o] = lv[4 * rt + g];
+                    part_i[o] = li[4 * rt + g];
+                }
+            }
+    }
+}
+
+// Reduces the partial lists of each (bank, query) to its top-k: one wave per query.
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float *__restrict__ part_v,
+                                                         const int *__restrict__ part_i, long queries, int slots, int k,
+                                                         float *__restrict__ vals, int *__restrict__ idx) {
+    const int lane = threadIdx.x & 63;
+    const long qy = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (qy >= queries) return;
+    float lv = -INFINITY;
+    int li = INT32_MAX;
+    const float *pv = part_v + (size_t)qy * slots * k;
+    const int *pi = part_i + (size_t)qy * slots * k;
+    const long total = (long)slots * k;
+    for (long base = 0; base < total; base += 64) {
+        const long e = base + lane;
+        const bool ok = e < total;
+        const float v = ok ? pv[e] : -INFINITY;
+        const int id = ok ? pi[e] : INT32_MAX;
+        const float tv = __shfl(lv, k - 1, 64);
+        const int ti = __shfl(li, k - 1, 64);
+        uint64_t m = __ballot(ok && id != INT32_MAX && topk_better(v, id, tv, ti));
+        while (m) {
+            const int src = __builtin_ctzll(m);
+            m &= m - 1;
+            topk_insert(lv, li, __shfl(v, src, 64), __shfl(id, src, 64), lane);
+        }
+    }
+    if (lane < k) {
+        vals[(size_t)qy * k + lane] = lv;
+        idx[(size_t)qy * k + lane] = li;
+    }
+}
+
+}  // namespace tq

@@ -144,3 +144,29 @@ def check_scores(got: np.ndarray, ref: np.ndarray, what: str = "scores"):
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} beyond tolerance; "
                            f"worst excess {np.max(err - tol):.3e}, max err {err.max():.3e}")
     return float(err.max())
+
+
+def check_topk(vals: np.ndarray, idx: np.ndarray, ref: np.ndarray, k: int, what: str = "topk"):
+    """Top-k protocol on one bank. vals/idx [G, k] from the GPU, ref [G, n] oracle
+    estimates on the same bank bytes. Every returned index must be a true top-k member
+    up to the score tolerance (oracle score >= s_k - tol(s_k), s_k the oracle's k-th best),
+    every returned value must match the oracle's estimate for its index (score
+    tolerance), and a list must be distinct indices, best first. Returns the fraction of
+    returned indices that equal the oracle's own top-k (ties by lower index)."""
+    G, n = ref.shape
+    idx = np.asarray(idx, np.int64)
+    vals = np.asarray(vals, np.float64)
+    assert idx.shape == (G, k) and vals.shape == (G, k)
+    assert ((idx >= 0) & (idx < n)).all(), f"{what}: index out of range"
+    order = np.lexsort((np.arange(n)[None, :].repeat(G, 0), -ref), axis=1)[:, :k]
+    sk = np.take_along_axis(ref, order[:, k - 1:k], axis=1)
+    got_ref = np.take_along_axis(ref, idx, axis=1)
+    tol_k = SCORE_ATOL + SCORE_RTOL * np.abs(sk)
+    assert (got_ref >= sk - tol_k).all(), (f"{what}: returned index below the k-th best by "
+                                           f"{np.max(sk - tol_k - got_ref):.3e}")
+    check_scores(vals, got_ref, f"{what} values")
+    for g in range(G):
+        assert len(set(idx[g].tolist())) == k, f"{what}: repeated index in query {g}"
+    assert (np.diff(vals, axis=1) <= 0).all(), f"{what}: list not best first"
+    same = np.mean([len(set(idx[g].tolist()) & set(order[g].tolist())) / k for g in range(G)])
+    return float(same)

@@ -1,0 +1,153 @@
+"""GPU top-k and the large-operand scorer (vector-search shapes, many queries) against
+the CPU oracle, through the C ABI. Small cases are compared on oracle-encoded banks
+(identical bank bytes on both sides); the full 2,000,000 x 768 database is encoded on
+the GPU and checked on sampled queries, the oracle scoring every key of the GPU's bank
+for them."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import both_params, check_encode, check_scores, check_topk, download_bank, upload_bank
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_inner_amd as tq
+
+    return tq
+
+
+def _oracle_bank(tq, cfg, bits, keys, layer=0):
+    gpu, orc = both_params(cfg, bits, layer)
+    refs = [oracle.encode(orc, keys[b]) for b in range(keys.shape[0])]
+    bank = upload_bank(tq, gpu, np.stack([r[0] for r in refs]), np.stack([r[1] for r in refs]),
+                       np.stack([r[2] for r in refs]), keys.shape[1])
+    return gpu, orc, refs, bank
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_encode_search_small(tq, bits):
+    """768-dimensional unit vectors: GPU encoding against the oracle's, record by record."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    n = 301
+    say(f"encode search-shaped d=768 b={bits} n={n}")
+    keys = workloads.keys(cfg, n=n)
+    gpu, orc = both_params(cfg, bits)
+    bank = tq.Bank(gpu, 1, n)
+    tq.tq_encode(gpu, torch.from_numpy(keys).cuda(), bank)
+    gb = download_bank(bank)
+    rep = {}
+    check_encode((gb[0][0], gb[1][0], gb[2][0]), oracle.encode_trace(orc, keys[0]), orc, n, rep)
+    say("   report", rep)
+
+
+@pytest.mark.parametrize("bits,n,G,k", [(4, 5003, 37, 10), (2, 3001, 9, 10), (4, 700, 5, 64), (2, 900, 3, 1)])
+def test_topk_search_small(tq, bits, n, G, k):
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    say(f"topk search-shaped: d=768 b={bits} n={n} G={G} k={k}")
+    keys = workloads.keys(cfg, n=n)
+    q = workloads.queries(cfg, G=G)
+    gpu, orc, refs, bank = _oracle_bank(tq, cfg, bits, keys)
+    vals, idx = tq.tq_topk(gpu, bank, torch.from_numpy(q).cuda(), k)
+    ref = oracle.score(orc, *refs[0], n, q[0])
+    same = check_topk(vals.cpu().numpy()[0], idx.cpu().numpy()[0], ref, k)
+    say(f"   returned indices equal to the oracle's top-{k}: {same:.4f}")
+
+
+def test_topk_several_banks_decode_shapes(tq):
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    n, k = 1000, 10
+    say("topk decode-shaped banks: 3 banks x 1000, G=4, b=3")
+    keys = workloads.keys(cfg, n=n, banks=[0, 9, 17])
+    q = workloads.queries(cfg, banks=[0, 9, 17])
+    gpu, orc, refs, bank = _oracle_bank(tq, cfg, 3, keys)
+    vals, idx = tq.tq_topk(gpu, bank, torch.from_numpy(q).cuda(), k)
+    for b in range(3):
+        ref = oracle.score(orc, *refs[b], n, q[b])
+        check_topk(vals.cpu().numpy()[b], idx.cpu().numpy()[b], ref, k, f"bank {b}")
+
+
+def test_topk_ties_by_lower_index(tq):
+    """Duplicate keys give equal estimates: the lower index must come first."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    n, k = 640, 12
+    keys = workloads.keys(cfg, n=n)
+    keys[0, 300:310] = keys[0, 5]  # ten copies of key 5 later in the bank
+    q = workloads.queries(cfg, G=4)
+    q[0, 0] = keys[0, 5]  # a query whose best match is key 5 and its copies
+    gpu, orc, refs, bank = _oracle_bank(tq, cfg, 4, keys)
+    vals, idx = tq.tq_topk(gpu, bank, torch.from_numpy(q).cuda(), k)
+    ref = oracle.score(orc, *refs[0], n, q[0])
+    check_topk(vals.cpu().numpy()[0], idx.cpu().numpy()[0], ref, k)
+    first = idx.cpu().numpy()[0, 0, :11].tolist()
+    assert first == [5] + list(range(300, 310)), first
+
+
+@pytest.mark.parametrize("cfg_name,bits,n,G", [("decode3b", 3, 777, 40), ("search", 4, 1500, 4), ("search", 2, 333, 21)])
+def test_score_large_operands(tq, cfg_name, bits, n, G):
+    """tq_score where the operands go through LDS: more than 16 queries per bank, or
+    768-dimensional keys."""
+    import torch
+
+    cfg = workloads.CONFIGS[cfg_name]
+    say(f"score {cfg_name} b={bits} n={n} G={G}")
+    banks = [0] if cfg.banks == 1 else [0, 1]
+    keys = workloads.keys(cfg, n=n, banks=banks)
+    q = workloads.queries(cfg, banks=banks, G=G)
+    gpu, orc, refs, bank = _oracle_bank(tq, cfg, bits, keys)
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+    for b in range(len(banks)):
+        say("   max err", check_scores(got[b], oracle.score(orc, *refs[b], n, q[b]), f"bank {b}"))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_topk_full_search_sampled(tq, bits):
+    """2,000,000 x 768 unit vectors encoded on the GPU, 1024 queries, top-10; the oracle
+    scores all 2,000,000 keys of the GPU's bank for sampled queries. Recall@10 against the
+    exact inner products is reported (no pin: the pages print none)."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    n, k = cfg.tokens, cfg.topk
+    say(f"full search b={bits}: {n} x {cfg.d}, G={cfg.G}, k={k}")
+    gpu, orc = both_params(cfg, bits)
+    keys = workloads.keys_device(cfg, 0, "cuda")
+    q = workloads.queries_device(cfg, 0, "cuda")
+    bank = tq.Bank(gpu, 1, n)
+    tq.tq_encode(gpu, keys, bank)
+    vals, idx = tq.tq_topk(gpu, bank, q, k)
+    torch.cuda.synchronize()
+    # recall@10 against exact fp32 inner products
+    exact = torch.topk(q[0] @ keys[0].T, k, dim=1).indices
+    hits = (idx[0].long()[:, :, None] == exact[:, None, :]).any(dim=2).float().mean().item()
+    say(f"   recall@{k} vs exact inner products: {hits:.4f}")
+    del keys
+    torch.cuda.empty_cache()
+    gb = download_bank(bank)
+    qh = q.cpu().numpy()
+    g = np.random.default_rng(bits)
+    for qi in g.choice(cfg.G, 6, replace=False):
+        ref = oracle.score(orc, gb[0][0], gb[1][0], gb[2][0], n, qh[0, qi:qi + 1])
+        same = check_topk(vals.cpu().numpy()[0, qi:qi + 1], idx.cpu().numpy()[0, qi:qi + 1], ref, k, f"query {qi}")
+        say(f"   query {qi}: overlap with the oracle's top-{k} {same:.2f}")

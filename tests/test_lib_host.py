@@ -108,6 +108,11 @@ def test_workspace_sizes(tq):
     assert p.workspace_bytes(tq.TQ_OP_SCORE, 64, 32768, 0) == 0
     assert p.workspace_bytes(tq.TQ_OP_TOPK, 1, 1000, 16, 10) > p.workspace_bytes(tq.TQ_OP_SCORE, 1, 1000, 16)
     assert p.workspace_bytes(tq.TQ_OP_TOPK, 1, 1000, 16, 65) == 0
+    # search shapes: the top-k partial lists come on top of the query operands
+    v = _with_fake_ptrs(tq, d=768, m=768, groups=((768, 3),))
+    t = v.workspace_bytes(tq.TQ_OP_TOPK, 1, 2_000_000, 1024, 10)
+    assert t > v.workspace_bytes(tq.TQ_OP_SCORE, 1, 2_000_000, 1024) and t % 256 == 0
+    assert v.workspace_bytes(tq.TQ_OP_TOPK, 1, 2_000_000, 1024, 64) > t
     # a valid shape without a compiled scorer layout
     q = _with_fake_ptrs(tq, d=160, m=128, groups=((160, 2),))
     assert q.workspace_bytes(tq.TQ_OP_SCORE, 1, 100, 4) == 0
@@ -167,6 +172,12 @@ def test_argument_validation_returns_before_any_launch(tq):
                      None) == tq.TQ_ERR_ARG
     assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 0, 0x2000, 0x3000, 0x4000, 1 << 20,
                      None) == tq.TQ_ERR_ARG
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 65, 0x2000, 0x3000, 0x4000, 1 << 20,
+                     None) == tq.TQ_ERR_ARG
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4000, 64,
+                     None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4001, 1 << 20,
+                     None) == tq.TQ_ERR_WORKSPACE
     assert L.tq_fp32_logits(None, 1, 10, 128, 0x1000, 4, 0x2000, None) == tq.TQ_ERR_ARG
     assert L.tq_copy(0x1001, 0x2000, 64, None) == tq.TQ_ERR_ARG
     # empty inputs are valid no-ops
