@@ -107,7 +107,7 @@ class Sweep:
         self.ws = tq.score_workspace(self.params, self.banks[0], cfg.G)
         self.scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
 
-    def step(self, tq, events=None):
+    def step(self, tq):
         """One decode step: per layer, one tq_score call (query preparation fused into the
         packed-key scorer: a single kernel launch). The C entry point is called with
         pre-marshalled arguments so that host-side Python overhead stays below the GPU time
@@ -123,14 +123,8 @@ class Sweep:
                                            stream))
                            for l in range(self.layers)]
         for score, sa in self._calls:
-            if events is not None:
-                e0, e1 = events.pop()
-                e0.record()
             if score(*sa):
                 raise RuntimeError("tq_score failed")
-            if events is not None:
-                e1.record()
-                events.done.append((e0, e1))
 
 
 class EventPool(list):
@@ -144,20 +138,29 @@ class EventPool(list):
         self.done = []
 
 
-def timed(fn, steps, warmup, launches_per_step):
+def timed(fn, steps, warmup, layers):
+    """Runs `warmup` untimed steps, then `steps` timed ones between synchronizations.
+    fn() runs one step (`layers` back-to-back launches on the current stream); a HIP event
+    pair on that stream brackets every timed step, so the mean launch duration is the
+    bracketed time over the launches inside it (an event pair around each launch would
+    add its own gap between the kernels). Returns (wall seconds, per-launch ms list)."""
     import torch
 
     for _ in range(warmup):
-        fn(None)
+        fn()
     torch.cuda.synchronize()
-    events = EventPool(steps * launches_per_step)
+    events = EventPool(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        fn(events)
+        e0, e1 = events.pop()
+        e0.record()
+        fn()
+        e1.record()
+        events.done.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in events.done]
+    kern_ms = [a.elapsed_time(b) / layers for a, b in events.done]
     return wall, kern_ms
 
 
@@ -197,6 +200,130 @@ def cpu_baseline(cfg, bits, banks, layers):
                   f"oracle encode of those keys {t_enc:.1f}s ({banks * n / t_enc:.3g} keys/s)",
         "encode_keys_per_s": banks * n / t_enc,
     }
+
+
+def copy_ceiling(tq, device, nbytes, copies=4, reps=12):
+    """Plain device copy moving the same total bytes as one score launch (half read, half
+    written), cycled over `copies` distinct buffer pairs so that no launch is served from
+    the 256 MB last-level cache: the HBM rate a streaming kernel of this size can reach on
+    this device."""
+    import torch
+
+    half = (nbytes // 2 + 15) // 16 * 16
+    src = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(copies)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(copies)]
+    for i in range(copies):
+        tq.tq_copy(src[i], dst[i])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r, (a, b) in enumerate(ev):
+        a.record()
+        tq.tq_copy(src[r % copies], dst[r % copies])
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {"bytes": 2 * half, "ms": ms, "gbps": 2 * half / (ms * 1e-3) / 1e9}
+
+
+def longctx_extra(tq, device):
+    """Long-context workload (8 banks x 131072 keys, two channel groups): encode rate, and
+    score rate over 12 distinct copies of the banks cycled (about 600 MB, beyond the
+    256 MB last-level cache, so every launch streams from HBM)."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["longctx"]
+    prm = params_for(tq, cfg, 3, device)
+    keys = workloads.keys_device(cfg, 0, device)
+    q = workloads.queries_device(cfg, 0, device)
+    bank = tq.Bank(prm, cfg.banks, cfg.tokens, device)
+    ws = torch.empty(prm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), dtype=torch.uint8, device=device)
+    tq.tq_encode(prm, keys, bank, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+    for a, b in ev:
+        a.record()
+        tq.tq_encode(prm, keys, bank, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    enc_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    copies = []
+    for _ in range(12):
+        c = tq.Bank(prm, cfg.banks, cfg.tokens, device)
+        c.bits.copy_(bank.bits)
+        c.norms.copy_(bank.norms)
+        c.rnorms.copy_(bank.rnorms)
+        copies.append(c)
+    scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+    sws = tq.score_workspace(prm, bank, cfg.G)
+    for c in copies[:2]:
+        tq.tq_score(prm, c, q, scores=scores, workspace=sws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(24)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        tq.tq_score(prm, copies[i % 12], q, scores=scores, workspace=sws)
+        b.record()
+    torch.cuda.synchronize()
+    sc_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    _, _, bpk = prm.layout(cfg.tokens)
+    keys_n = cfg.banks * cfg.tokens
+    return {
+        "workload": "longctx: 8 banks x 131072 bf16 keys, groups (32 ch, 2-bit codebook) + (96 ch, 1-bit), "
+                    "one 128-row sign sketch, G=4",
+        "bytes_per_key": int(bpk),
+        "encode_keys_per_s": keys_n / (enc_ms * 1e-3),
+        "encode_ms": enc_ms,
+        "score_pairs_per_s": keys_n * cfg.G / (sc_ms * 1e-3),
+        "score_ms": sc_ms,
+        "score_gbps": keys_n * (bpk + 4 * cfg.G) / (sc_ms * 1e-3) / 1e9,
+    }
+
+
+def search_extra(tq, device):
+    """Vector search: 2,000,000 x 768 unit vectors, 1024 queries, top-10 per query, at
+    b=4 and b=2; encode rate, top-k rate and recall@10 against the exact inner products."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["search"]
+    out = {"workload": "search: 2,000,000 x 768 fp32 unit vectors, 1024 unit queries, top-10, m=768"}
+    for bits in (4, 2):
+        prm = params_for(tq, cfg, bits, device)
+        keys = workloads.keys_device(cfg, 0, device)
+        q = workloads.queries_device(cfg, 0, device)
+        bank = tq.Bank(prm, 1, cfg.tokens, device)
+        ews = torch.empty(prm.workspace_bytes(tq.TQ_OP_ENCODE, 1, cfg.tokens), dtype=torch.uint8, device=device)
+        tq.tq_encode(prm, keys, bank, workspace=ews)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tq.tq_encode(prm, keys, bank, workspace=ews)
+        b.record()
+        torch.cuda.synchronize()
+        enc_ms = a.elapsed_time(b)
+        exact = torch.topk(q[0] @ keys[0].T, cfg.topk, dim=1).indices
+        del keys
+        torch.cuda.empty_cache()
+        ws = torch.empty(prm.workspace_bytes(tq.TQ_OP_TOPK, 1, cfg.tokens, cfg.G, cfg.topk), dtype=torch.uint8,
+                         device=device)
+        tq.tq_topk(prm, bank, q, cfg.topk, workspace=ws)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in ev:
+            a.record()
+            vals, idx = tq.tq_topk(prm, bank, q, cfg.topk, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        tk_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        recall = (idx[0].long()[:, :, None] == exact[:, None, :]).any(dim=2).float().mean().item()
+        pairs = cfg.tokens * cfg.G
+        out[f"b{bits}"] = {
+            "encode_keys_per_s": cfg.tokens / (enc_ms * 1e-3),
+            "encode_ms": enc_ms,
+            "topk_ms": tk_ms,
+            "topk_pairs_per_s": pairs / (tk_ms * 1e-3),
+            "topk_tflops_algorithmic": pairs * 2 * (cfg.d + cfg.m) / (tk_ms * 1e-3) / 1e12,
+            "recall_at_10_vs_exact": recall,
+        }
+        del bank, ws, exact
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -240,7 +367,7 @@ def main():
     log(f"encode: {enc_ms:.2f} ms for {keys_total} keys")
 
     log("timed sweep b=3")
-    wall, kern_ms = timed(lambda ev: sw3.step(tq, ev), args.steps, args.warmup, L)
+    wall, kern_ms = timed(lambda: sw3.step(tq), args.steps, args.warmup, L)
     ms_per_step = 1e3 * wall / args.steps
     pairs_per_step = cfg.banks * cfg.tokens * cfg.G * L
     value = pairs_per_step / (wall / args.steps)
@@ -273,16 +400,17 @@ def main():
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_fused_kernel",
+            "kernel": "score_ring_kernel",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": counters_for("score_fused_kernel", "decode8b_b3"),
+            "traffic": counters_for("score_ring_kernel", "decode8b_b3"),
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms": kavg,
-            "launches": len(kern_ms),
+            "launches": len(kern_ms) * L,
         },
+        "hbm_copy_ceiling": copy_ceiling(tq, device, bytes_per_launch),
         "encode": {
             "keys_per_s": keys_total / (enc_ms * 1e-3),
             "ms_total": enc_ms,
@@ -296,7 +424,7 @@ def main():
     if not args.no_extras:
         log("b=4 sweep")
         sw4 = Sweep(tq, cfg, 4, L, device)
-        wall4, kern4 = timed(lambda ev: sw4.step(tq, ev), max(args.steps // 2, 1), 2, L)
+        wall4, kern4 = timed(lambda: sw4.step(tq), max(args.steps // 2, 1), 2, L)
         b4_bytes = cfg.banks * cfg.tokens * (sw4.bytes_per_key + 4 * cfg.G)
         out["b4"] = {
             "value": pairs_per_step / (wall4 / max(args.steps // 2, 1)),
@@ -314,15 +442,9 @@ def main():
         qf = [workloads.queries_device(cfg, l, device) for l in range(nfp)]
         sf = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
 
-        def fp32_step(ev):
+        def fp32_step():
             for layer in range(L):
-                if ev is not None:
-                    e0, e1 = ev.pop()
-                    e0.record()
                 tq.tq_fp32_logits(kf[layer % nfp], qf[layer % nfp], sf)
-                if ev is not None:
-                    e1.record()
-                    ev.done.append((e0, e1))
 
         wallf, kernf = timed(fp32_step, max(args.steps // 4, 1), 1, L)
         fbytes = cfg.banks * cfg.tokens * (4 * cfg.d + 4 * cfg.G)
@@ -334,6 +456,13 @@ def main():
             "context": "the pages quote up to 8x for 4-bit keys vs 32-bit keys on H100",
         }
         del kf
+        torch.cuda.empty_cache()
+
+        log("long-context mixed bit widths")
+        out["longctx"] = longctx_extra(tq, device)
+        torch.cuda.empty_cache()
+        log("vector search top-10")
+        out["search"] = search_extra(tq, device)
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

@@ -128,11 +128,11 @@ int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, in
  * operands; same write-up, usage example: the query stays at full precision).
  * q (device) float32 [banks][G][d]. Writes the prepared operands into
  * `workspace` (device), of tq_workspace_bytes(TQ_OP_SCORE, ...) bytes, for
- * tq_score_prepared / tq_topk_prepared. */
+ * tq_score_prepared (tq_score and tq_topk run it themselves when they need it). */
 int tq_prepare_queries(const tq_params *p, const float *q, int64_t banks, int32_t G, void *workspace,
                        size_t ws_bytes, void *stream);
 
-/* Estimated inner products of prepared queries against packed banks:
+/* Estimated inner products of prepared queries (any G) against packed banks:
  *   est = sum_g (nu_g / sqrt(d_g)) <R_g q_g, c_g[idx_g]>
  *       + sqrt(pi/2) / m * rho * <S q, 2*signs - 1>
  * (turboquant-pytorch write-up: stage 2 makes this estimate unbiased; usage
@@ -142,15 +142,24 @@ int tq_prepare_queries(const tq_params *p, const float *q, int64_t banks, int32_
 int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, int32_t G,
                       const void *workspace, float *scores, void *stream);
 
-/* tq_prepare_queries followed by tq_score_prepared. */
+/* The same estimates from unprepared queries q (device) float32 [banks][G][d]. For up
+ * to 16 queries per bank and operands that fit in registers the preparation runs inside
+ * the scoring kernel (one launch) and `workspace` is not touched; otherwise this is
+ * tq_prepare_queries followed by tq_score_prepared and `workspace` (device) must hold
+ * tq_workspace_bytes(TQ_OP_SCORE, ...) bytes, 256-byte aligned. */
 int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G,
              float *scores, void *workspace, size_t ws_bytes, void *stream);
 
 /* Per query, the k largest estimates (vector search over the packed database;
  * tambur.pub article, vector-search paragraph), largest first, equal estimates
- * by lower key index. vals (device) float32 [banks][G][k], idx (device) int32
- * [banks][G][k]. 1 <= k <= 64 and k <= n. The score rows are never written to
- * memory. Workspace: tq_workspace_bytes(TQ_OP_TOPK, ...). */
+ * by lower key index; the estimates are those tq_score returns (fp32), ranked as
+ * fp32. vals (device) float32 [banks][G][k], idx (device) int32 [banks][G][k].
+ * q (device) float32 [banks][G][d], any G >= 1. 1 <= k <= 64 and k <= n, else
+ * TQ_ERR_ARG. The score rows are never written to memory: the prepared query
+ * operands and the per-wave partial top-k lists live in `workspace` (device) of
+ * tq_workspace_bytes(TQ_OP_TOPK, ...) bytes, 256-byte aligned (TQ_ERR_WORKSPACE
+ * otherwise). TQ_ERR_UNSUPPORTED for a layout whose operands exceed 150 KiB of LDS
+ * per row of four queries. */
 int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G, int32_t k,
             float *vals, int32_t *idx, void *workspace, size_t ws_bytes, void *stream);
 

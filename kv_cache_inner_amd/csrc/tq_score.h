@@ -45,24 +45,46 @@ constexpr int prep_chunks(int d) {
 // whose plain base-256 digits minus 128 are the limbs. The additive constant is formed from
 // the same fp32 weights, so the integer part and the constant stay consistent.
 template <class L, int RT>
-struct PrepScratch {
+struct PrepDims {
     static constexpr int NR = L::D + L::M;
     static constexpr int CPR = prep_chunks(L::D);  // column chunks per matrix row (power of two)
     static constexpr int RB = 64 / CPR;            // matrix rows per wave in the product
-    float qv[L::D][4 * RT];                        // queries, column-major
-    float qg[L::D][4 * RT];                        // columns in group order (qg[pos] = column chan[pos])
-    float w[4 * RT][NR];                           // R_g q_g (group order) then S q
-    float pmax[NR / RB][4 * RT];                   // per row-block max |w|
-    double psum[NR / RB][4 * RT];                  // per row-block sum of w
+};
+
+// LDS scratch of the query preparation, as one block.
+template <class L, int RT>
+struct PrepScratch {
+    using PD = PrepDims<L, RT>;
+    float qsrc[2][L::D][4 * RT];         // [0]: queries column-major; [1]: columns in group order
+    float w[4 * RT][PD::NR];             // R_g q_g (group order) then S q
+    float pmax[PD::NR / PD::RB][4 * RT];   // per row-block max |w|
+    double psum[PD::NR / PD::RB][4 * RT];  // per row-block sum of w
     int F[4 * RT][L::NCLS];
 };
+
+// The scratch arrays by reference: members of one PrepScratch, or separate LDS arrays
+// (which the compiler can tell apart from LDS written by direct-to-LDS loads).
+template <class L, int RT>
+struct PrepView {
+    using PD = PrepDims<L, RT>;
+    float (&qsrc)[2][L::D][4 * RT];
+    float (&w)[4 * RT][PD::NR];
+    float (&pmax)[PD::NR / PD::RB][4 * RT];
+    double (&psum)[PD::NR / PD::RB][4 * RT];
+    int (&F)[4 * RT][L::NCLS];
+};
+
+template <class L, int RT>
+__device__ __forceinline__ PrepView<L, RT> view_of(PrepScratch<L, RT> &s) {
+    return PrepView<L, RT>{s.qsrc, s.w, s.pmax, s.psum, s.F};
+}
 
 // One GEMV item of the query preparation: (row tile, matrix row, part). Part p of a row
 // takes the float4 columns p, p+CPR, ... so that the CPR lanes of a row read contiguous
 // 16*CPR-byte runs.
 template <class L, int RT>
 struct PrepItem {
-    static constexpr int NR = PrepScratch<L, RT>::NR, CPR = PrepScratch<L, RT>::CPR;
+    static constexpr int NR = PrepDims<L, RT>::NR, CPR = PrepDims<L, RT>::CPR;
     static constexpr int CH = L::D / CPR;  // columns per chunk
     const float *row;
     int K, off, part, r, qb;
@@ -147,22 +169,41 @@ __device__ __forceinline__ void prep_barrier() {
         __syncthreads();
 }
 
-struct NoHook {
-    __device__ __forceinline__ void operator()() const {}
+// Where the preparation writes its outputs: a flat byte array (the global workspace, or a
+// block of LDS), or LDS arrays of one row tile reached by typed indexing.
+template <class L>
+struct OperandPtr {
+    int8_t *frags;   // [RT][NF][64][16 B]
+    double *consts;  // [4 RT][NCLS][2]
+    __device__ __forceinline__ uint32_t &frag(int rt, int f, int ln, int v) const {
+        return *reinterpret_cast<uint32_t *>(frags + ((((size_t)rt * L::NF + f) * 64 + ln) * 16 + 4 * v));
+    }
+    __device__ __forceinline__ double &cst(int qq, int c, int k) const {
+        return consts[((size_t)qq * L::NCLS + c) * 2 + k];
+    }
 };
 
-// The staging and the GEMV use NT threads; the exponent and fragment phases use the
-// threads below NT_TAIL whose tail_worker is set, the others only take part in the
-// barriers. `after_gemv` runs in every thread right after the barrier that ends the GEMV,
-// when no thread reads the query staging or the matrix chunks any more.
-template <class L, int RT, int NT, bool LDS_ONLY = false, int NT_TAIL = NT, class Hook = NoHook>
+template <class L>
+struct OperandLds {
+    uint32_t (&frags)[L::NF][64][4];
+    double (&consts)[4][L::NCLS][2];
+    __device__ __forceinline__ uint32_t &frag(int, int f, int ln, int v) const { return frags[f][ln][v]; }
+    __device__ __forceinline__ double &cst(int qq, int c, int k) const { return consts[qq][c][k]; }
+};
+
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+// `hook(k)` runs in every thread right after the k-th of the three work-group barriers
+// (k = 1, 2, 3), for work that can interleave with the preparation.
+template <class L, int RT, int NT, bool LDS_ONLY = false, class Out = OperandPtr<L>, class Hook = NoHook>
 __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int tid, const float *__restrict__ q, long bank,
                                             int G, int q0, const float *__restrict__ rot,
                                             const float *__restrict__ proj, const int *__restrict__ chan,
-                                            const PrepArgs &pa, PrepScratch<L, RT> &ps, int8_t *frag_out,
-                                            double *const_out, Hook after_gemv = Hook{},
-                                            bool tail_worker = true) {
-    using PS = PrepScratch<L, RT>;
+                                            const PrepArgs &pa, const PrepView<L, RT> &ps, const Out &out,
+                                            Hook hook = Hook{}) {
+    using PS = PrepDims<L, RT>;
     using PI = PrepItem<L, RT>;
     constexpr int NQ4 = 4 * RT;
     constexpr int NR = PS::NR, CPR = PS::CPR, RB = PS::RB;
@@ -178,16 +219,18 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
             a = gq < G ? qrow[c] : 0.0f;
             b = gq < G ? qrow[chan ? chan[c] : c] : 0.0f;
         }
-        ps.qv[c][qq] = a;
-        ps.qg[c][qq] = b;
+        ps.qsrc[0][c][qq] = a;
+        ps.qsrc[1][c][qq] = b;
     }
     prep_barrier<LDS_ONLY>();
+    hook(1);
     // GEMV items; parts of a row sit in adjacent lanes, rows of a wave form one row block;
     // both are reduced with shuffles in a fixed order.
     for (int it = tid; it < NR * RT * CPR; it += NT) {
         const PI pi(it, rot, proj);
         const int part = pi.part, r = pi.r, qb = pi.qb;
-        const float(*src)[NQ4] = pi.rotated ? ps.qg + pi.off : ps.qv;  // operand columns of this row
+        // operand columns of this row (one array, indexed: no choice between two objects)
+        const float(*src)[NQ4] = ps.qsrc[pi.rotated ? 1 : 0] + (pi.rotated ? pi.off : 0);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         {
             f32x4 m[CH / 4];
@@ -243,9 +286,9 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
             }
     }
     prep_barrier<LDS_ONLY>();
-    after_gemv();
+    hook(2);
     // per (query, term): exponent F from the max |weight|, additive constant from the sum
-    for (int it = tid; tail_worker && it < NQ4 * L::NCLS; it += NT_TAIL) {
+    for (int it = tid; it < NQ4 * L::NCLS; it += NT) {
         const int qq = it / L::NCLS, c = it % L::NCLS, gq = q0 + qq;
         const int r0 = c < L::NG ? (c ? L::D0 : 0) : L::D;
         const int r1 = c < L::NG ? (c ? L::D : L::D0) : NR;
@@ -271,14 +314,14 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
         if (wmax > 0.0) frexp(wmax, &e);  // wmax < 2^e
         const int F = wmax > 0.0 ? 30 - e : 0;
         ps.F[qq][c] = F;
-        double *o = const_out + ((size_t)qq * L::NCLS + c) * 2;
-        o[0] = ldexp(1.0, -F);
-        o[1] = gq < G ? (c < L::NG ? -(c ? pa.cmax[1] : pa.cmax[0]) * sm : -sm) : 0.0;
+        out.cst(qq, c, 0) = ldexp(1.0, -F);
+        out.cst(qq, c, 1) = gq < G ? (c < L::NG ? -(c ? pa.cmax[1] : pa.cmax[0]) * sm : -sm) : 0.0;
     }
     prep_barrier<LDS_ONLY>();
+    hook(3);
     // fragments: RT waves per fragment (wave-uniform fragment id); item (gl, query, dword v)
     // -> 4 K positions x 4 limbs (one dword in each of four lanes)
-    for (int fw = wv; tail_worker && fw < L::NF * RT; fw += NT_TAIL / 64) {
+    for (int fw = wv; fw < L::NF * RT; fw += NT / 64) {
         const int fr = fw / RT, it = (fw % RT) * 64 + lane;
         const int v = it & 3, qq = (it >> 2) % NQ4, gl = (it >> 2) / NQ4;
         static_for<L::NF>([&](auto fcst) {
@@ -310,14 +353,13 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
                 if (t == 7) V = -V;  // the byte 0x80 reads as -128
                 U[e] = (uint32_t)V + 0x80808080u;
             }
-            const int rt = qq / 4;
-            int8_t *base = frag_out + (((size_t)rt * L::NF + f) * 64 + 16 * gl + 4 * (qq % 4)) * 16 + 4 * v;
+            const int rt = qq / 4, ln0 = 16 * gl + 4 * (qq % 4);
 #pragma unroll
             for (int limb = 0; limb < 4; ++limb) {
                 uint32_t packed = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) packed |= (((U[e] >> (8 * limb)) & 0xFFu) ^ 0x80u) << (8 * e);
-                *reinterpret_cast<uint32_t *>(base + limb * 16) = packed;
+                out.frag(rt, f, ln0 + limb, v) = packed;
             }
         });
     }
@@ -330,7 +372,8 @@ __device__ __forceinline__ void prep_operands(int tid, const float *__restrict__
                                               PrepScratch<L, RT> &ps, int8_t *frag_out, double *const_out) {
     PrepRegs<L, RT, NT> pr;
     prep_load<L, RT, NT>(pr, tid, q, bank, G, q0, rot, proj, chan);
-    prep_finish<L, RT, NT>(pr, tid, q, bank, G, q0, rot, proj, chan, pa, ps, frag_out, const_out);
+    prep_finish<L, RT, NT>(pr, tid, q, bank, G, q0, rot, proj, chan, pa, view_of(ps),
+                           OperandPtr<L>{frag_out, const_out});
 }
 
 // Standalone query preparation: one 1024-thread work-group per (bank, row tile of 4 queries).
@@ -601,8 +644,8 @@ __global__ __launch_bounds__(fused_waves<RT>() * 64) void score_fused_kernel(
     asm volatile("" ::: "memory");
     TileBatch<L, TB> A, B;
     ts.prefetch(A, B);
-    prep_finish<L, RT, WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, lds.ps, &lds.frags[0][0][0][0],
-                                   &lds.consts[0][0][0]);
+    prep_finish<L, RT, WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, view_of(lds.ps),
+                                   OperandPtr<L>{&lds.frags[0][0][0][0], &lds.consts[0][0][0]});
     __syncthreads();
     if (t0 >= t1) return;
     i8x16 wf[RT][L::NF];
@@ -708,7 +751,16 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks, long n, int n_tiles, int G,
     int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
     using RTL = RingTile<L>;
-    __shared__ FusedLds<L, 1> lds;
+    using PD = PrepDims<L, 1>;
+    // the preparation's scratch, operands and ring as separate LDS arrays: LDS accesses to
+    // the first ones then never wait for direct-to-LDS loads into the ring
+    __shared__ float s_qsrc[2][L::D][4];
+    __shared__ float s_w[4][PD::NR];
+    __shared__ float s_pmax[PD::NR / PD::RB][4];
+    __shared__ double s_psum[PD::NR / PD::RB][4];
+    __shared__ int s_F[4][L::NCLS];
+    __shared__ __attribute__((aligned(16))) uint32_t s_frags[L::NF][64][4];
+    __shared__ double s_consts[4][L::NCLS][2];
     __shared__ __attribute__((aligned(16))) uint32_t ring_mem[RING_WAVES][S][RTL::WORDS];
     const long bank = blockIdx.x / wgs_per_bank;
     const int part = blockIdx.x % wgs_per_bank;
@@ -724,39 +776,35 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     const float *rb = rnorms + (size_t)bank * n_pad;
     float *ob = scores + (size_t)bank * G * n;
     lds_u32 *ring = (lds_u32 *)&ring_mem[wv][0][0];
+    const NormLane<L> nl(nb, rb, lane);
 
-    // Prologue. All waves load and stage the query and run the GEMV from registers (one
-    // matrix chunk per thread). After the GEMV barrier the upper half of the waves issues
-    // the ring fill of every wave (its partner's first, then its own) while the lower half
-    // finishes the operands: those waves have no direct-to-LDS loads pending, so none of
-    // their LDS accesses waits on the fill. Before the last barrier each filler waits for
-    // its partner's fill (issued first, so its own stays in flight).
-    constexpr int HALF = RING_WAVES / 2;
-    const bool filler = wv >= HALF;
-    const int tlast = max(t1 - 1, 0);
+    // Prologue. Every wave first requests and consumes its share of the preparation's
+    // global reads (loads complete in issue order, and a load consumed while a direct-to-LDS
+    // load is pending would wait for that too). It then fills its own ring in four pieces,
+    // one before the preparation and one after each of its barriers, so that the fill
+    // streams from HBM while the operands are built and no phase stalls on issuing it.
     PrepRegs<L, 1, RING_WAVES * 64> pr;
     prep_load<L, 1, RING_WAVES * 64>(pr, tid, q, bank, G, 0, rot, proj, chan);
-    auto fill = [&]() {
-        if (!filler) return;
-        const int pv = wv - HALF;  // partner wave: same split of the work-group's tiles
-        const int pt0 = min(w0 + pv * per, w1), pt1 = min(pt0 + per, w1), plast = max(pt1 - 1, 0);
-        lds_u32 *pring = (lds_u32 *)&ring_mem[pv][0][0];
-        const NormLane<L> nl(nb, rb, lane);
-        // slots past a short run reload its last tile, so the fill has no branches
+    asm volatile("" : "+v"(pr.qv), "+v"(pr.qg));
 #pragma unroll
-        for (int i = 0; i < S; ++i) {
-            const int t = min(pt0 + i, plast);
-            ring_fetch<L>(tile_bits<L>(bb, t), nl.at(t), pring + i * RTL::WORDS, lane);
-        }
+    for (int k = 0; k < PrepRegs<L, 1, RING_WAVES * 64>::PRE; ++k)
 #pragma unroll
-        for (int i = 0; i < S; ++i) {
-            const int t = min(t0 + i, tlast);
-            ring_fetch<L>(tile_bits<L>(bb, t), nl.at(t), ring + i * RTL::WORDS, lane);
-        }
+        for (int i = 0; i < PrepItem<L, 1>::CH / 4; ++i) asm volatile("" : "+v"(pr.m[k][i]));
+    asm volatile("" ::: "memory");
+    const int tlast = max(t1 - 1, 0);
+    // slots past a short run reload its last tile, so the fill has no branches
+    auto fill_piece = [&](int piece) {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if (i * 4 / S == piece) {
+                const int t = min(t0 + i, tlast);
+                ring_fetch<L>(tile_bits<L>(bb, t), nl.at(t), ring + i * RTL::WORDS, lane);
+            }
     };
-    prep_finish<L, 1, RING_WAVES * 64, true, HALF * 64>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, lds.ps,
-                                                        &lds.frags[0][0][0][0], &lds.consts[0][0][0], fill, !filler);
-    if (filler) __builtin_amdgcn_s_waitcnt(waitcnt_vm(S * RTL::LOADS));
+    fill_piece(0);
+    PrepView<L, 1> view{s_qsrc, s_w, s_pmax, s_psum, s_F};
+    prep_finish<L, 1, RING_WAVES * 64, true>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, view,
+                                             OperandLds<L>{s_frags, s_consts}, fill_piece);
     lds_barrier();
     if (nt <= 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -764,7 +812,7 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     }
     i8x16 wf[1][L::NF];
 #pragma unroll
-    for (int f = 0; f < L::NF; ++f) wf[0][f] = *reinterpret_cast<const i8x16 *>(&lds.frags[0][f][lane][0]);
+    for (int f = 0; f < L::NF; ++f) wf[0][f] = *reinterpret_cast<const i8x16 *>(&s_frags[f][lane][0]);
     // per-term constants with the term's scale folded in: est = sum_c s_c (S_c cs_c + ck_c),
     // s_c = nu_g for the code terms of group g and rho for the sketch term
     double cs[L::NCLS], ck[L::NCLS];
@@ -772,8 +820,8 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
         constexpr int c = decltype(cc)::value;
         constexpr int g = c < L::NG ? c : 0;
         const double f = c < L::NG ? sc.inv_sqrt_d[g] : sc.qjl;
-        cs[c] = lds.consts[gl][c][0] * f;
-        ck[c] = lds.consts[gl][c][1] * f;
+        cs[c] = s_consts[gl][c][0] * f;
+        ck[c] = s_consts[gl][c][1] * f;
     });
     // per-lane word offsets inside a slot (lane group gl takes word 4s+gl of key j)
     int woff[L::NSQ];
@@ -783,19 +831,38 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
         wlive[s] = 4 * s + gl < L::W;
         woff[s] = (wlive[s] ? 4 * s + gl : 0) * 16 + j;
     }
-    const NormLane<L> nl(nb, rb, lane);
 
-    auto read_slot = [&](const volatile lds_u32 *slot, uint32_t(&sw)[L::NSQ], float(&nu)[L::NG], float &rho) {
+    // A slot's words for this lane, read in one asm block that ends with its own wait: the
+    // compiler sees no LDS access there that it could order against the ring's direct-to-LDS
+    // loads, so the only waits on those are the explicit ones above. Lane group gl takes
+    // word 4s+gl of key j (words past the tile's W are read from the slot's later rows and
+    // dropped); norms of key j; residual norm of key j.
+    static_assert(4 * L::NSQ <= RingTile<L>::ROWS && L::NSQ <= 4 && L::NG <= 2, "slot read layout");
+    const uint32_t lane_w = 4u * lane, lane_n = 4u * j * L::NG, lane_r = 4u * j;
+    auto read_slot = [&](const lds_u32 *slot, uint32_t(&sw)[L::NSQ], float(&nu)[L::NG], float &rho) {
+        const uint32_t base = (uint32_t)(uintptr_t)slot;
+        uint32_t w[4], nn[2], r;
+        constexpr int O1 = (L::NSQ > 1 ? 1 : 0) * 256, O2 = (L::NSQ > 2 ? 2 : 0) * 256,
+                      O3 = (L::NSQ > 3 ? 3 : 0) * 256, ON = 64 * L::W, ON1 = 64 * L::W + (L::NG > 1 ? 4 : 0),
+                      OR = 64 * (L::W + L::NG);
+        asm volatile(
+            "ds_read_b32 %0, %7\n"
+            "ds_read_b32 %1, %7 offset:%10\n"
+            "ds_read_b32 %2, %7 offset:%11\n"
+            "ds_read_b32 %3, %7 offset:%12\n"
+            "ds_read_b32 %4, %8 offset:%13\n"
+            "ds_read_b32 %5, %8 offset:%14\n"
+            "ds_read_b32 %6, %9 offset:%15\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(nn[0]), "=&v"(nn[1]), "=&v"(r)
+            : "v"(base + lane_w), "v"(base + lane_n), "v"(base + lane_r), "i"(O1), "i"(O2), "i"(O3), "i"(ON),
+              "i"(ON1), "i"(OR)
+            : "memory");
 #pragma unroll
-        for (int s = 0; s < L::NSQ; ++s) sw[s] = slot[woff[s]];
+        for (int s = 0; s < L::NSQ; ++s) sw[s] = wlive[s] ? w[s] : 0u;
 #pragma unroll
-        for (int g = 0; g < L::NG; ++g) nu[g] = __uint_as_float(slot[16 * L::W + j * L::NG + g]);
-        rho = __uint_as_float(slot[16 * (L::W + L::NG) + j]);
-        // the slot's reads are done before the next tile's loads overwrite it
-        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
-#pragma unroll
-        for (int s = 0; s < L::NSQ; ++s)
-            if (!wlive[s]) sw[s] = 0u;
+        for (int g = 0; g < L::NG; ++g) nu[g] = __uint_as_float(nn[g]);
+        rho = __uint_as_float(r);
     };
     auto tile_est = [&](const uint32_t(&sw)[L::NSQ], const float(&nu)[L::NG], float rho) -> float {
         i32x4 acc[1][L::NCLS];

@@ -271,3 +271,38 @@ def test_encode_full_decode8b_layer_sampled(tq):
         rep = {}
         check_encode((gathered, gn, gr), oracle.encode_trace(orc, sk), orc, 2048, rep)
         say("report", rep)
+
+
+def test_longctx_full_size_sampled(tq):
+    """Long-context workload at full size (8 banks x 131072 bf16 keys, two channel groups
+    at 2 and 1 codebook bits, one 128-row sketch): GPU encoding on 2048 sampled keys and
+    GPU scores on sampled pairs, both against the oracle."""
+    import torch
+
+    cfg = workloads.CONFIGS["longctx"]
+    gpu, orc = both_params(cfg, 3)
+    keys = workloads.keys_device(cfg, 0, "cuda")
+    q = workloads.queries_device(cfg, 0, "cuda")
+    say(f"longctx full size: {cfg.banks} x {cfg.tokens}")
+    bank = tq.Bank(gpu, cfg.banks, cfg.tokens)
+    tq.tq_encode(gpu, keys, bank)
+    scores = tq.tq_score(gpu, bank, q).cpu().numpy()
+    g = np.random.default_rng(4)
+    bi = g.integers(0, cfg.banks, 2048)
+    ki = g.integers(0, cfg.tokens, 2048)
+    ki[:2] = [0, cfg.tokens - 1]
+    bt, kt = torch.from_numpy(bi).cuda(), torch.from_numpy(ki).cuda()
+    sk = keys[bt, kt].float().cpu().numpy()
+    gbits = bank.bits[bt, kt // 16, :, kt % 16].cpu().numpy().view(np.uint32)
+    gathered = np.ascontiguousarray(gbits.reshape(128, 16, -1).transpose(0, 2, 1))
+    rep = {}
+    check_encode((gathered, bank.norms[bt, kt].cpu().numpy(), bank.rnorms[bt, kt].cpu().numpy()),
+                 oracle.encode_trace(orc, sk), orc, 2048, rep)
+    say("report", rep)
+    gb = download_bank(bank)
+    qh = q.cpu().numpy()
+    for b in g.choice(cfg.banks, 4, replace=False):
+        kk = np.concatenate([g.integers(0, cfg.tokens, 400), [0, cfg.tokens - 1]])
+        qi = g.integers(0, cfg.G, len(kk))
+        ref = oracle.score_pairs(orc, gb[0][b], gb[1][b], gb[2][b], qh[b], qi, kk)
+        check_scores(scores[b, qi, kk], ref, f"bank {b}")
