@@ -24,6 +24,17 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// Work-group barrier over LDS traffic only: it waits for this wave's LDS operations but not
+// for its vector-memory loads, so loads issued earlier (direct-to-LDS or into registers)
+// stay in flight (a __syncthreads() would drain them all). Only for code whose cross-wave
+// communication goes through ordinary LDS reads and writes.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Estimator scale constants of one call, passed by value.
 struct ScoreScale {
     double inv_sqrt_d[2];  // 1/sqrt(d_g)

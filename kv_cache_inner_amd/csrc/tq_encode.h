@@ -235,4 +235,275 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Register-resident encoder for d <= 128 and m <= 128 (KV-cache key shapes).
+//
+// The rotation and the projection are dense contractions with small, fixed right-hand
+// matrices, so a persistent work-group of 8 waves keeps them in registers for the whole
+// launch as MFMA A operands: wave w holds the rotation rows of its 16 rotated coordinates
+// 16w..16w+15 (group order) and rows 16w..16w+15 of S'. It then walks 16-key tiles:
+//   - the keys sit in LDS in the B-operand order of v_mfma_f32_16x16x4f32 (lane 16k+i of
+//     K-step s holds coordinate 4s+k of key i), so every operand read is one conflict-free
+//     ds_read_b128 that serves four K-steps;
+//   - each wave rotates its 16 coordinates of the 16 keys (K = d_g), buckets them and
+//     writes the residual back to LDS in the same operand order;
+//   - each wave projects the residual on its 16 rows of S' (K = d) and keeps the signs;
+//   - bit-planes and sign bits are gathered across lanes into the tile's stored words in
+//     LDS and leave as one coalesced block.
+// The keys of the work-group's next tile are loaded one tile ahead; two LDS-only barriers
+// per tile. Arithmetic per element is that of encode_kernel (fp32 products and sums in
+// the same K order, fp64 norms, the same bucket and residual formulas).
+constexpr int ENCR_WAVES = 8, ENCR_DMAX = 128, ENCR_WMAX = 16;
+
+// LDS float offset of (coordinate pos, key) in the B-operand layout [pos/16][64 lanes][4]
+__device__ __forceinline__ int encr_off(int pos, int key) {
+    return ((((pos >> 4) << 6) + ((pos & 3) << 4) + key) << 2) + ((pos >> 2) & 3);
+}
+
+// Four consecutive channels of one key, as loaded (one 16- or 8-byte load).
+template <typename KT>
+struct KeyQuad;
+template <>
+struct KeyQuad<float> {
+    u32x4 v;
+    __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
+    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const u32x4 *>(p); }
+    __device__ __forceinline__ float get(int u) const { return __uint_as_float(v[u]); }
+};
+template <>
+struct KeyQuad<uint16_t> {
+    uint32_t v0, v1;
+    __device__ __forceinline__ void zero() { v0 = v1 = 0; }
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        const uint2 t = *reinterpret_cast<const uint2 *>(p);
+        v0 = t.x;
+        v1 = t.y;
+    }
+    __device__ __forceinline__ float get(int u) const {
+        const uint32_t w = u < 2 ? v0 : v1;
+        return __uint_as_float((u & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// acc = A * B over NS K-steps: A from registers (a[s], lane (k, i) of K-step s), B from
+// the LDS operand layout (b[(s/4)*64] holds K-steps s..s+3 of this lane)
+template <int NS>
+__device__ __forceinline__ f32x4 encr_mma(const float (&a)[32], const f32x4 *b) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s4 = 0; s4 < NS / 4; ++s4) {
+        const f32x4 v = b[s4 * 64];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 0], v[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 1], v[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 2], v[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 3], v[3], acc, 0, 0, 0);
+    }
+    return acc;
+}
+// the same for a wave-uniform K-step count ns in {8, 16, 24, 32} (a group of 32..128
+// coordinates)
+__device__ __forceinline__ f32x4 encr_mma_n(int ns, const float (&a)[32], const f32x4 *b) {
+    switch (ns) {
+        case 8: return encr_mma<8>(a, b);
+        case 16: return encr_mma<16>(a, b);
+        case 24: return encr_mma<24>(a, b);
+        default: return encr_mma<32>(a, b);
+    }
+}
+
+template <typename KT>
+__global__ __launch_bounds__(ENCR_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void encode_regs_kernel(
+    const KT *__restrict__ keys, long n, int n_tiles, long total_tiles, const float *__restrict__ rot,
+    const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
+    float *__restrict__ norms, float *__restrict__ rnorms) {
+    __shared__ __align__(16) float Xf[ENCR_DMAX * 16];
+    __shared__ __align__(16) float Uf[ENCR_DMAX * 16];
+    __shared__ __align__(16) uint32_t TW[2][ENCR_WMAX * 16];
+    __shared__ float s_inv[2][16][2], s_coef[2][16][2];
+    __shared__ float s_cent[2][8];
+    __shared__ double s_rho[ENCR_WAVES][16];
+    __shared__ int s_pos[ENCR_DMAX];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 15, q = lane >> 4;
+    const int D = a.d, M = a.m, ng = a.ng;
+    const long n_pad = (long)n_tiles * 16;
+    const int grid = gridDim.x;
+
+    // channel -> coordinate position in group order (entries of a non-permutation are
+    // kept in range)
+    for (int c = tid; c < ENCR_DMAX; c += ENCR_WAVES * 64) s_pos[c] = c < D ? c : 0;
+    if (tid < 16) s_cent[tid >> 3][tid & 7] = a.cent[tid >> 3][tid & 7];
+    __syncthreads();
+    if (chan)
+        for (int p = tid; p < D; p += ENCR_WAVES * 64) {
+            const int c = chan[p];
+            if ((unsigned)c < (unsigned)D) s_pos[c] = p;
+        }
+    __syncthreads();
+
+    // this thread's share of a tile's keys: key ik, channels 4cq..4cq+3
+    const int ik = tid >> 5, cq = tid & 31;
+    const bool cq_live = 4 * cq < D;
+    // lanes cq = 0, 1 finish the norms of groups 0, 1 (read once here: a lane-dependent
+    // choice between kernel arguments inside the loop becomes a memory load)
+    const double my_sqrt_d = cq == 1 ? a.sqrt_d[1] : a.sqrt_d[0];
+    int xo[4];
+    bool in_g1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int pos = cq_live ? s_pos[4 * cq + u] : 0;
+        xo[u] = encr_off(pos, ik);
+        in_g1[u] = ng > 1 && pos >= a.gdim[0];
+    }
+
+    // rotation operand: rows j0..j0+15 of R_g, lane (q, i) holds R_g[j0+i][4s+q]
+    const int pos0 = 16 * wv;
+    const bool rot_live = pos0 < D;
+    const int g = (ng > 1 && pos0 >= a.gdim[0]) ? 1 : 0;
+    const int dg = g ? a.gdim[1] : a.gdim[0];
+    const int off = g ? a.goff[1] : 0;
+    const int j0 = pos0 - off, nsr = dg / 4;
+    float ra[32];
+    {
+        const float *Rg = rot + (g ? (size_t)a.gdim[0] * a.gdim[0] : 0) + (size_t)(j0 + i) * dg + q;
+#pragma unroll
+        for (int s = 0; s < 32; ++s) ra[s] = (rot_live && s < nsr) ? Rg[4 * s] : 0.0f;
+    }
+    float th[7];
+    const int nb = g ? a.gbits[1] : a.gbits[0];
+#pragma unroll
+    for (int t = 0; t < 7; ++t) th[t] = t < (1 << nb) - 1 ? (g ? a.thr[1][t] : a.thr[0][t]) : INFINITY;
+    const int cw_word = (g ? a.gword[1] : a.gword[0]) + (j0 >> 5), cw_half = (j0 >> 4) & 1, wpp = dg / 32;
+
+    // projection operand: rows r0..r0+15 of S', lane (q, i) holds S'[r0+i][4s+q]
+    const int r0 = 16 * wv;
+    const bool prj_live = r0 < M;
+    const int nsp = D / 4;
+    float rp[32];
+    {
+        const float *Sp = sp + (size_t)(r0 + i) * D + q;
+#pragma unroll
+        for (int s = 0; s < 32; ++s) rp[s] = (prj_live && s < nsp) ? Sp[4 * s] : 0.0f;
+    }
+    const int sw_word = a.sword + (r0 >> 5), sw_half = (r0 >> 4) & 1;
+
+    auto load_keys = [&](long T, KeyQuad<KT> &kq) {
+        kq.zero();
+        if (T < total_tiles && cq_live) {
+            const long bank = T / n_tiles, key = (T % n_tiles) * 16 + ik;
+            if (key < n) kq.load(keys + ((size_t)bank * n + key) * D + 4 * cq);
+        }
+    };
+    // keys -> LDS operand order; per-group norms (fp64 sums of exact float squares)
+    auto stage = [&](long T, const KeyQuad<KT> &kq, int buf) {
+        double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float v = kq.get(u);
+            if (cq_live) Xf[xo[u]] = v;
+            const double dv = v;
+            if (in_g1[u])
+                s1 += dv * dv;
+            else
+                s0 += dv * dv;
+        }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            s0 += __shfl_xor(s0, o, 64);
+            s1 += __shfl_xor(s1, o, 64);
+        }
+        if (cq < ng) {
+            const double s = cq ? s1 : s0, sd = my_sqrt_d;
+            const double nu = sqrt(s);
+            const float nu_s = (float)nu;
+            s_inv[buf][ik][cq] = nu > 0.0 ? (float)(sd / nu) : 0.0f;
+            s_coef[buf][ik][cq] = (float)((double)nu_s / sd);
+            const long bank = T / n_tiles, key = (T % n_tiles) * 16 + ik;
+            norms[((size_t)bank * n_pad + key) * ng + cq] = nu_s;
+        }
+    };
+
+    long T = blockIdx.x;
+    KeyQuad<KT> kq;
+    load_keys(T, kq);
+    stage(T, kq, 0);
+    load_keys(T + grid, kq);
+    lds_barrier();
+    uint16_t *const tw16 = reinterpret_cast<uint16_t *>(&TW[0][0]);
+    for (int it = 0; T < total_tiles; T += grid, ++it) {
+        const int buf = it & 1;
+        const long bank = T / n_tiles;
+        const int tile = (int)(T % n_tiles);
+        // stage 1: rotate, bucket, residual
+        if (rot_live) {
+            const f32x4 acc = encr_mma_n(nsr, ra, reinterpret_cast<const f32x4 *>(Xf) + (off >> 4) * 64 + lane);
+            const float inv = s_inv[buf][i][g], coef = s_coef[buf][i][g];
+            double rr = 0.0;
+            uint32_t pl01 = 0, pl2 = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float y = acc[r];
+                const float z = y * inv;
+                int idx = 0;
+#pragma unroll
+                for (int t = 0; t < 7; ++t) idx += z >= th[t] ? 1 : 0;
+                const float u = y - coef * s_cent[g][idx];
+                Uf[((wv * 64 + 16 * r + i) << 2) + q] = u;
+                rr += (double)u * (double)u;
+                pl01 |= ((uint32_t)(idx & 1) << r) | ((uint32_t)((idx >> 1) & 1) << (16 + r));
+                pl2 |= (uint32_t)((idx >> 2) & 1) << r;
+            }
+            pl01 <<= 4 * q;
+            pl2 <<= 4 * q;
+            pl01 |= __shfl_xor(pl01, 16, 64);
+            pl2 |= __shfl_xor(pl2, 16, 64);
+            rr += __shfl_xor(rr, 16, 64);
+            pl01 |= __shfl_xor(pl01, 32, 64);
+            pl2 |= __shfl_xor(pl2, 32, 64);
+            rr += __shfl_xor(rr, 32, 64);
+            if (q == 0) s_rho[wv][i] = rr;
+            // bit-plane p of these 16 coordinates is written by lane group p
+            if (q < nb) {
+                const uint32_t v = q == 0 ? (pl01 & 0xffffu) : (q == 1 ? (pl01 >> 16) : pl2);
+                tw16[((buf * ENCR_WMAX * 16) + (cw_word + q * wpp) * 16 + i) * 2 + cw_half] = (uint16_t)v;
+            }
+        } else if (lane < 16) {
+            s_rho[wv][lane] = 0.0;
+        }
+        lds_barrier();
+        // the next tile's keys (loaded one tile ago) into the now free key buffer
+        const long Tn = T + grid;
+        if (Tn < total_tiles) {
+            stage(Tn, kq, buf ^ 1);
+            load_keys(Tn + grid, kq);
+        }
+        // stage 2: project the residual, keep the signs
+        if (prj_live) {
+            const f32x4 acc = encr_mma_n(nsp, rp, reinterpret_cast<const f32x4 *>(Uf) + lane);
+            uint32_t sg = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sg |= (acc[r] >= 0.0f ? 1u : 0u) << r;
+            sg <<= 4 * q;
+            sg |= __shfl_xor(sg, 16, 64);
+            sg |= __shfl_xor(sg, 32, 64);
+            if (q == 0) tw16[((buf * ENCR_WMAX * 16) + sw_word * 16 + i) * 2 + sw_half] = (uint16_t)sg;
+        }
+        // residual norm rho = |u| (fp64 sum of the waves' partial sums)
+        if (wv == ENCR_WAVES - 1 && lane < 16) {
+            double s = 0.0;
+#pragma unroll
+            for (int w = 0; w < ENCR_WAVES; ++w) s += s_rho[w][lane];
+            rnorms[(size_t)bank * n_pad + (size_t)tile * 16 + lane] = (float)sqrt(s);
+        }
+        lds_barrier();
+        // the tile's stored words: bits[bank][tile][W][16], one coalesced block
+        if (tid < a.W * 4)
+            reinterpret_cast<u32x4 *>(bits + (size_t)T * a.W * 16)[tid] =
+                reinterpret_cast<const u32x4 *>(&TW[buf][0])[tid];
+    }
+}
+
 }  // namespace tq

@@ -150,17 +150,6 @@ __device__ __forceinline__ void prep_load(PrepRegs<L, RT, NT> &pr, int tid, cons
         if (tid + k * NT < PR::ITEMS) PrepItem<L, RT>(tid + k * NT, rot, proj).load(pr.m[k]);
 }
 
-// Work-group barrier over LDS traffic only: it waits for this wave's LDS operations but not
-// for its vector-memory loads, so direct-to-LDS loads issued earlier stay in flight (a
-// __syncthreads() would drain them: it orders them as pending LDS writes). Only for code
-// whose cross-wave communication goes through ordinary LDS reads and writes.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 template <bool LDS_ONLY>
 __device__ __forceinline__ void prep_barrier() {
     if constexpr (LDS_ONLY)
