@@ -237,29 +237,47 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
 
 
 // ---------------------------------------------------------------------------------------
-// Register-resident encoder for d <= 128 and m <= 128 (KV-cache key shapes).
+// Encoder for d <= 128 and m <= 128 (KV-cache key shapes) on the bf16 matrix cores.
 //
-// The rotation and the projection are dense contractions with small, fixed right-hand
-// matrices, so a persistent work-group of 8 waves keeps them in registers for the whole
-// launch as MFMA A operands: wave w holds the rotation rows of its 16 rotated coordinates
-// 16w..16w+15 (group order) and rows 16w..16w+15 of S'. It then walks 16-key tiles:
-//   - the keys sit in LDS in the B-operand order of v_mfma_f32_16x16x4f32 (lane 16k+i of
-//     K-step s holds coordinate 4s+k of key i), so every operand read is one conflict-free
-//     ds_read_b128 that serves four K-steps;
-//   - each wave rotates its 16 coordinates of the 16 keys (K = d_g), buckets them and
-//     writes the residual back to LDS in the same operand order;
-//   - each wave projects the residual on its 16 rows of S' (K = d) and keeps the signs;
-//   - bit-planes and sign bits are gathered across lanes into the tile's stored words in
-//     LDS and leave as one coalesced block.
-// The keys of the work-group's next tile are loaded one tile ahead; two LDS-only barriers
-// per tile. Arithmetic per element is that of encode_kernel (fp32 products and sums in
-// the same K order, fp64 norms, the same bucket and residual formulas).
-constexpr int ENCR_WAVES = 8, ENCR_DMAX = 128, ENCR_WMAX = 16;
+// The rotation and the projection are dense contractions with small fixed matrices, done
+// here in bf16 MFMA (v_mfma_f32_16x16x32_bf16) at fp32-level accuracy: an fp32 value is
+// exactly the sum of three bf16 values (x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0
+// - x1): 8 significant bits each, every difference exact), products of bf16 values are
+// exact in fp32 and the MFMA accumulates in fp32. So
+//   - the rotation of bf16 keys by R = R0 + R1 + R2 is three MFMAs per 32-deep K block
+//     with nothing dropped (six, with pieces of the key, for fp32 keys);
+//   - the projection of the fp32 residual U = U0 + U1 + U2 by S' = S'0 + S'1 + S'2 takes
+//     the six piece products of order a + b <= 2; each dropped one is below 2^-26 of the
+//     leading product.
+// The error left is fp32 accumulation rounding, as with fp32 MFMA; unlike fp32 MFMA (which
+// issues at the vector fp32 rate), the bf16 matrix instructions run beside vector work.
+//
+// A persistent work-group of 16 waves walks 16-key tiles in a two-stage pipeline with one
+// LDS barrier per tile:
+//   - waves 0..7 keep rotation rows (three pieces) of coordinates 16w..16w+15 (group
+//     order) as MFMA A operands in registers; for tile t they rotate, bucket, and write
+//     the residual pieces to LDS in B-operand order, plus the tile's code bit-planes;
+//   - waves 8..15 keep rows 16(w-8).. of S' (three pieces); for tile t-1 they project the
+//     residual and add the sign words, stage tile t+1's keys into LDS (B-operand order)
+//     with their norms, finish tile t-1's residual norms and store tile t-2's words.
+// MFMA operand layout (16x16x32): lane 16k+i holds row i, K elements 8k..8k+7 of its block
+// for A; column i, the same K elements for B; the result rows are 4k..4k+3 of column i.
+//
+// Per-element vector work is kept small, since it bounds the encoder:
+//   - bucket = number of thresholds <= z, counted from the sign bits of z - t (no compare
+//     and condition-register round trips); the planes come from the same sign words;
+//   - norms: fp32 squares (exact for bf16 keys), four per lane summed in turn, then a
+//     fixed pairwise tree across the 32 lanes of a key (DPP and row swaps): every term
+//     passes through at most 8 roundings, so |x|^2 is within 8 units of fp32 rounding
+//     (relative) of the exact sum of non-negative terms, far inside 1e-6 on |x|;
+//   - residual norm: per-wave fp32 partial sums over 16 coordinates, combined in fp64;
+//   - cross-lane gathers of bit nibbles and partial sums use v_permlane16/32_swap.
+constexpr int ENCS_WAVES = 16, ENCS_ROT = 8, ENCS_DMAX = 128, ENCS_WMAX = 16;
 
-// LDS float offset of (coordinate pos, key) in the B-operand layout [pos/16][64 lanes][4]
-__device__ __forceinline__ int encr_off(int pos, int key) {
-    return ((((pos >> 4) << 6) + ((pos & 3) << 4) + key) << 2) + ((pos >> 2) & 3);
-}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Four consecutive channels of one key, as loaded (one 16- or 8-byte load).
 template <typename KT>
@@ -286,223 +304,392 @@ struct KeyQuad<uint16_t> {
     }
 };
 
-// acc = A * B over NS K-steps: A from registers (a[s], lane (k, i) of K-step s), B from
-// the LDS operand layout (b[(s/4)*64] holds K-steps s..s+3 of this lane)
-template <int NS>
-__device__ __forceinline__ f32x4 encr_mma(const float (&a)[32], const f32x4 *b) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s4 = 0; s4 < NS / 4; ++s4) {
-        const f32x4 v = b[s4 * 64];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 0], v[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 1], v[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 2], v[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s4 + 3], v[3], acc, 0, 0, 0);
-    }
-    return acc;
+
+// v moved across lanes by a DPP pattern (quad permutations, row mirrors): every source lane
+// exists, so each lane receives exactly one value
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-// the same for a wave-uniform K-step count ns in {8, 16, 24, 32} (a group of 32..128
-// coordinates)
-__device__ __forceinline__ f32x4 encr_mma_n(int ns, const float (&a)[32], const f32x4 *b) {
-    switch (ns) {
-        case 8: return encr_mma<8>(a, b);
-        case 16: return encr_mma<16>(a, b);
-        case 24: return encr_mma<24>(a, b);
-        default: return encr_mma<32>(a, b);
+// x[lane] op x[lane ^ 16] and x[lane] op x[lane ^ 32], as the two outputs of a row swap
+__device__ __forceinline__ uint32_t or_rows16(uint32_t x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return p[0] | p[1];
+}
+__device__ __forceinline__ uint32_t or_rows32(uint32_t x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return p[0] | p[1];
+}
+__device__ __forceinline__ float add_rows16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_rows32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sum over the 32 lanes of a half-wave by a fixed pairwise tree (xor 1, xor 2, 8-lane
+// mirror, 16-lane mirror, row swap); every lane of the half ends with the same value.
+__device__ __forceinline__ float sum_half_wave(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    return add_rows16(v);
+}
+
+// Buckets and residuals of one lane's four rotated coordinates (MFMA output rows r) of
+// one key, for a codebook of NB bits. th: the 2^NB - 1 ascending thresholds. Returns the
+// bit-plane nibbles: bit r of pl[p] = bit p of bucket r.
+template <int NB>
+__device__ __forceinline__ void encr_bucket(const f32x4 &acc, float inv, float coef, const float (&th)[7],
+                                            const float *cent, float (&u)[4], uint32_t (&pl)[3]) {
+    constexpr int NT = (1 << NB) - 1;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) pl[p] = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float y = acc[r];
+        const float z = y * inv;
+        // sign bit of z - t is set iff z < t (z - t is +0 when z == t)
+        uint32_t sw[NT];
+        uint32_t below = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sw[t] = __float_as_uint(z - th[t]);
+            below += sw[t] >> 31;
+        }
+        const uint32_t idx = NT - below;
+        u[r] = y - coef * cent[idx];
+        // bit p of the bucket, from the sign words (bucket = number of thresholds <= z)
+        uint32_t b0, b1 = 0, b2 = 0;
+        if constexpr (NB == 1) {
+            b0 = ~sw[0];
+        } else if constexpr (NB == 2) {
+            b1 = ~sw[1];
+            b0 = ~(sw[0] ^ sw[1] ^ sw[2]);
+        } else {
+            b2 = ~sw[3];
+            b1 = ~(sw[1] ^ sw[3] ^ sw[5]);
+            b0 = ~(sw[0] ^ sw[1] ^ sw[2] ^ sw[3] ^ sw[4] ^ sw[5] ^ sw[6]);
+        }
+        pl[0] |= (b0 >> 31) << r;
+        if constexpr (NB > 1) pl[1] |= (b1 >> 31) << r;
+        if constexpr (NB > 2) pl[2] |= (b2 >> 31) << r;
     }
 }
 
+
+// (a, b) rounded to bf16 (v_cvt_pk_bf16_f32, round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// exact three-piece bf16 split of (a, b): a = lo(p0) + lo(p1) + lo(p2), b likewise (high)
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t &p0, uint32_t &p1, uint32_t &p2) {
+    p0 = pk_bf16(a, b);
+    a -= bf16_lo(p0);
+    b -= bf16_hi(p0);
+    p1 = pk_bf16(a, b);
+    a -= bf16_lo(p1);
+    b -= bf16_hi(p1);
+    p2 = pk_bf16(a, b);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// acc = A * B over NKB 32-deep K blocks. A: three bf16 pieces per block in registers.
+// B: from LDS at b[kb * 64] (piece 0) and b[p * ps + kb * 64] (pieces 1, 2 when XP == 3).
+// Smaller products first.
+template <int NKB, int XP>
+__device__ __forceinline__ f32x4 encs_mma(const u32x4 (&am)[4][3], const u32x4 *b, int ps) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 x0 = b[kb * 64];
+        if constexpr (XP == 1) {
+            acc = mfma_bf16(am[kb][2], x0, acc);
+            acc = mfma_bf16(am[kb][1], x0, acc);
+            acc = mfma_bf16(am[kb][0], x0, acc);
+        } else {
+            const u32x4 x1 = b[ps + kb * 64], x2 = b[2 * ps + kb * 64];
+            acc = mfma_bf16(am[kb][0], x2, acc);
+            acc = mfma_bf16(am[kb][1], x1, acc);
+            acc = mfma_bf16(am[kb][2], x0, acc);
+            acc = mfma_bf16(am[kb][0], x1, acc);
+            acc = mfma_bf16(am[kb][1], x0, acc);
+            acc = mfma_bf16(am[kb][0], x0, acc);
+        }
+    }
+    return acc;
+}
+// the same for a wave-uniform block count nkb in 1..4 (32..128 deep)
+template <int XP>
+__device__ __forceinline__ f32x4 encs_mma_n(int nkb, const u32x4 (&am)[4][3], const u32x4 *b, int ps) {
+    switch (nkb) {
+        case 1: return encs_mma<1, XP>(am, b, ps);
+        case 2: return encs_mma<2, XP>(am, b, ps);
+        case 3: return encs_mma<3, XP>(am, b, ps);
+        default: return encs_mma<4, XP>(am, b, ps);
+    }
+}
+
+// A operand of rows row0.. of a row-major fp32 matrix (row stride ld), K blocks kb < nkb
+// starting at column c0: lane (k, i) gets row row0 + i, columns c0 + 32kb + 8k .. + 7,
+// split into three bf16 pieces.
+__device__ __forceinline__ void encs_load_a(u32x4 (&am)[4][3], const float *mat, int ld, int row0, int c0, int nkb,
+                                            int lane) {
+    const float *src = mat + (size_t)(row0 + (lane & 15)) * ld + c0 + 8 * (lane >> 4);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t p0 = 0, p1 = 0, p2 = 0;
+            if (kb < nkb) split3_pair(src[32 * kb + 2 * d], src[32 * kb + 2 * d + 1], p0, p1, p2);
+            am[kb][0][d] = p0;
+            am[kb][1][d] = p1;
+            am[kb][2][d] = p2;
+        }
+    }
+}
+
+// bf16 element index, inside one piece of the LDS operand layout [kb][64 lanes][8], of
+// coordinate pos of key `key`
+__device__ __forceinline__ int encs_elem(int pos, int key) {
+    return ((((pos >> 5) << 6) + (((pos >> 3) & 3) << 4) + key) << 3) + (pos & 7);
+}
+
 template <typename KT>
-__global__ __launch_bounds__(ENCR_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) void encode_regs_kernel(
-    const KT *__restrict__ keys, long n, int n_tiles, long total_tiles, const float *__restrict__ rot,
+__global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
+    const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
     float *__restrict__ norms, float *__restrict__ rnorms) {
-    __shared__ __align__(16) float Xf[ENCR_DMAX * 16];
-    __shared__ __align__(16) float Uf[ENCR_DMAX * 16];
-    __shared__ __align__(16) uint32_t TW[2][ENCR_WMAX * 16];
+    constexpr int XP = sizeof(KT) == 2 ? 1 : 3;  // key pieces: bf16 keys are exact in one
+    constexpr int PS = 4 * 64;                     // piece stride of the operand buffers (u32x4)
+    __shared__ __align__(16) u32x4 XB[2][XP][4][64];
+    __shared__ __align__(16) u32x4 UB[2][3][4][64];
+    __shared__ __align__(16) uint32_t TW[3][ENCS_WMAX * 16];
     __shared__ float s_inv[2][16][2], s_coef[2][16][2];
     __shared__ float s_cent[2][8];
-    __shared__ double s_rho[ENCR_WAVES][16];
-    __shared__ int s_pos[ENCR_DMAX];
+    __shared__ float s_rho[2][ENCS_ROT][16];
+    __shared__ int s_pos[ENCS_DMAX];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, q = lane >> 4;
     const int D = a.d, M = a.m, ng = a.ng;
-    const long n_pad = (long)n_tiles * 16;
     const int grid = gridDim.x;
+    const bool rot_role = wv < ENCS_ROT;
 
     // channel -> coordinate position in group order (entries of a non-permutation are
     // kept in range)
-    for (int c = tid; c < ENCR_DMAX; c += ENCR_WAVES * 64) s_pos[c] = c < D ? c : 0;
+    for (int c = tid; c < ENCS_DMAX; c += ENCS_WAVES * 64) s_pos[c] = c < D ? c : 0;
     if (tid < 16) s_cent[tid >> 3][tid & 7] = a.cent[tid >> 3][tid & 7];
     __syncthreads();
     if (chan)
-        for (int p = tid; p < D; p += ENCR_WAVES * 64) {
+        for (int p = tid; p < D; p += ENCS_WAVES * 64) {
             const int c = chan[p];
             if ((unsigned)c < (unsigned)D) s_pos[c] = p;
         }
     __syncthreads();
 
-    // this thread's share of a tile's keys: key ik, channels 4cq..4cq+3
-    const int ik = tid >> 5, cq = tid & 31;
-    const bool cq_live = 4 * cq < D;
-    // lanes cq = 0, 1 finish the norms of groups 0, 1 (read once here: a lane-dependent
-    // choice between kernel arguments inside the loop becomes a memory load)
-    const double my_sqrt_d = cq == 1 ? a.sqrt_d[1] : a.sqrt_d[0];
-    int xo[4];
-    bool in_g1[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int pos = cq_live ? s_pos[4 * cq + u] : 0;
-        xo[u] = encr_off(pos, ik);
-        in_g1[u] = ng > 1 && pos >= a.gdim[0];
-    }
-
-    // rotation operand: rows j0..j0+15 of R_g, lane (q, i) holds R_g[j0+i][4s+q]
+    // ---- rotation role: coordinates pos0..pos0+15 of group g
     const int pos0 = 16 * wv;
-    const bool rot_live = pos0 < D;
+    const bool rot_live = rot_role && pos0 < D;
     const int g = (ng > 1 && pos0 >= a.gdim[0]) ? 1 : 0;
     const int dg = g ? a.gdim[1] : a.gdim[0];
     const int off = g ? a.goff[1] : 0;
-    const int j0 = pos0 - off, nsr = dg / 4;
-    float ra[32];
-    {
-        const float *Rg = rot + (g ? (size_t)a.gdim[0] * a.gdim[0] : 0) + (size_t)(j0 + i) * dg + q;
-#pragma unroll
-        for (int s = 0; s < 32; ++s) ra[s] = (rot_live && s < nsr) ? Rg[4 * s] : 0.0f;
-    }
-    float th[7];
+    const int j0 = pos0 - off, nkb_r = dg / 32;
     const int nb = g ? a.gbits[1] : a.gbits[0];
+    float th[7];
 #pragma unroll
     for (int t = 0; t < 7; ++t) th[t] = t < (1 << nb) - 1 ? (g ? a.thr[1][t] : a.thr[0][t]) : INFINITY;
     const int cw_word = (g ? a.gword[1] : a.gword[0]) + (j0 >> 5), cw_half = (j0 >> 4) & 1, wpp = dg / 32;
+    // this lane's residual slot: coordinates pos0 + 4q .. +3 of key i, as 4 bf16 of a piece
+    const int u_elem = encs_elem(pos0 + 4 * q, i);
 
-    // projection operand: rows r0..r0+15 of S', lane (q, i) holds S'[r0+i][4s+q]
-    const int r0 = 16 * wv;
-    const bool prj_live = r0 < M;
-    const int nsp = D / 4;
-    float rp[32];
-    {
-        const float *Sp = sp + (size_t)(r0 + i) * D + q;
-#pragma unroll
-        for (int s = 0; s < 32; ++s) rp[s] = (prj_live && s < nsp) ? Sp[4 * s] : 0.0f;
-    }
+    // ---- projection role: rows r0..r0+15 of S'
+    const int r0 = 16 * (wv - ENCS_ROT);
+    const bool prj_live = !rot_role && r0 < M;
+    const int nkb_p = D / 32;
     const int sw_word = a.sword + (r0 >> 5), sw_half = (r0 >> 4) & 1;
+
+    u32x4 am[4][3];
+    if (rot_live)
+        encs_load_a(am, rot + (g ? (size_t)a.gdim[0] * a.gdim[0] : 0), dg, j0, 0, nkb_r, lane);
+    else if (prj_live)
+        encs_load_a(am, sp, D, r0, 0, nkb_p, lane);
+
+    // ---- staging (projection-role threads): key ik, channels 4cq..4cq+3
+    const int st = tid - ENCS_ROT * 64;
+    const int ik = (st >> 5) & 15, cq = st & 31;
+    const bool cq_live = !rot_role && 4 * cq < D;
+    const float sqrt_d0 = (float)a.sqrt_d[0], sqrt_d1 = (float)a.sqrt_d[1];
+    const float inv_sqrt_d0 = (float)(1.0 / a.sqrt_d[0]), inv_sqrt_d1 = ng > 1 ? (float)(1.0 / a.sqrt_d[1]) : 0.0f;
+    int xo[4];
+    uint32_t in_g1 = 0;  // bit u: channel 4cq+u belongs to group 1
+    bool contig = true;  // the four channels land on four consecutive slots of one lane
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int pos = cq_live ? s_pos[4 * cq + u] : 4 * cq + u;
+        xo[u] = encs_elem(pos, ik);
+        in_g1 |= (ng > 1 && pos >= a.gdim[0]) ? 1u << u : 0u;
+        contig = contig && xo[u] == xo[0] + u;
+    }
+    contig = contig && (xo[0] & 3) == 0;
+    const int key_off = ik * D + 4 * cq;
 
     auto load_keys = [&](long T, KeyQuad<KT> &kq) {
         kq.zero();
-        if (T < total_tiles && cq_live) {
-            const long bank = T / n_tiles, key = (T % n_tiles) * 16 + ik;
-            if (key < n) kq.load(keys + ((size_t)bank * n + key) * D + 4 * cq);
+        if (T < total_tiles) {
+            const int bank = (int)T / n_tiles;
+            const long key0 = (long)((int)T - bank * n_tiles) * 16;
+            const KT *tile_keys = keys + ((size_t)bank * n + key0) * D;  // wave-uniform
+            if (cq_live && key0 + ik < n) kq.load(tile_keys + key_off);
         }
     };
-    // keys -> LDS operand order; per-group norms (fp64 sums of exact float squares)
+    // keys -> LDS operand order (pieces for fp32 keys); per-group norms
     auto stage = [&](long T, const KeyQuad<KT> &kq, int buf) {
-        double s0 = 0.0, s1 = 0.0;
+        float v[4], s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float v = kq.get(u);
-            if (cq_live) Xf[xo[u]] = v;
-            const double dv = v;
-            if (in_g1[u])
-                s1 += dv * dv;
-            else
-                s0 += dv * dv;
-        }
+        for (int u = 0; u < 4; ++u) v[u] = kq.get(u);
+        if (cq_live) {
+            uint16_t *xb = reinterpret_cast<uint16_t *>(&XB[buf][0][0][0]);
+            if constexpr (XP == 1) {
+                if (contig)
+                    *reinterpret_cast<u32x2 *>(xb + xo[0]) = u32x2{kq.v0, kq.v1};
+                else
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-            s0 += __shfl_xor(s0, o, 64);
-            s1 += __shfl_xor(s1, o, 64);
+                    for (int u = 0; u < 4; ++u) xb[xo[u]] = (uint16_t)(__float_as_uint(v[u]) >> 16);
+            } else {
+                uint32_t pa[3], pb[3];
+                split3_pair(v[0], v[1], pa[0], pa[1], pa[2]);
+                split3_pair(v[2], v[3], pb[0], pb[1], pb[2]);
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    uint16_t *xp = xb + p * PS * 8;
+                    if (contig) {
+                        *reinterpret_cast<u32x2 *>(xp + xo[0]) = u32x2{pa[p], pb[p]};
+                    } else {
+                        xp[xo[0]] = (uint16_t)pa[p];
+                        xp[xo[1]] = (uint16_t)(pa[p] >> 16);
+                        xp[xo[2]] = (uint16_t)pb[p];
+                        xp[xo[3]] = (uint16_t)(pb[p] >> 16);
+                    }
+                }
+            }
         }
+        if (ng > 1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool h = (in_g1 >> u) & 1;
+                s0 = fmaf(h ? 0.0f : v[u], v[u], s0);
+                s1 = fmaf(h ? v[u] : 0.0f, v[u], s1);
+            }
+            s1 = sum_half_wave(s1);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s0 = fmaf(v[u], v[u], s0);
+        }
+        s0 = sum_half_wave(s0);
         if (cq < ng) {
-            const double s = cq ? s1 : s0, sd = my_sqrt_d;
-            const double nu = sqrt(s);
-            const float nu_s = (float)nu;
-            s_inv[buf][ik][cq] = nu > 0.0 ? (float)(sd / nu) : 0.0f;
-            s_coef[buf][ik][cq] = (float)((double)nu_s / sd);
-            const long bank = T / n_tiles, key = (T % n_tiles) * 16 + ik;
-            norms[((size_t)bank * n_pad + key) * ng + cq] = nu_s;
+            const float s = cq ? s1 : s0;
+            const float nu = sqrtf(s);
+            s_inv[buf][ik][cq] = s > 0.0f ? (cq ? sqrt_d1 : sqrt_d0) / nu : 0.0f;
+            s_coef[buf][ik][cq] = nu * (cq ? inv_sqrt_d1 : inv_sqrt_d0);
+            norms[((size_t)T * 16 + ik) * ng + cq] = nu;  // bank * n_pad + key == 16 T + ik
         }
     };
 
-    long T = blockIdx.x;
+    const long T0 = blockIdx.x;
     KeyQuad<KT> kq;
-    load_keys(T, kq);
-    stage(T, kq, 0);
-    load_keys(T + grid, kq);
+    if (!rot_role) {
+        load_keys(T0, kq);
+        stage(T0, kq, 0);
+        load_keys(T0 + grid, kq);
+    }
     lds_barrier();
     uint16_t *const tw16 = reinterpret_cast<uint16_t *>(&TW[0][0]);
-    for (int it = 0; T < total_tiles; T += grid, ++it) {
-        const int buf = it & 1;
-        const long bank = T / n_tiles;
-        const int tile = (int)(T % n_tiles);
-        // stage 1: rotate, bucket, residual
-        if (rot_live) {
-            const f32x4 acc = encr_mma_n(nsr, ra, reinterpret_cast<const f32x4 *>(Xf) + (off >> 4) * 64 + lane);
-            const float inv = s_inv[buf][i][g], coef = s_coef[buf][i][g];
-            double rr = 0.0;
-            uint32_t pl01 = 0, pl2 = 0;
+    int tb = 0;  // it % 3
+    for (int it = 0;; ++it, tb = tb == 2 ? 0 : tb + 1) {
+        const long tr = T0 + (long)it * grid;  // rotated in this step
+        const long tp = tr - grid;             // projected
+        const long tw = tr - 2 * (long)grid;   // stored
+        if (tw >= total_tiles) break;
+        const int buf = it & 1, tb_p = tb == 0 ? 2 : tb - 1, tb_w = tb == 2 ? 0 : tb + 1;
+        if (rot_role) {
+            if (rot_live && tr < total_tiles) {
+                const f32x4 acc = encs_mma_n<XP>(nkb_r, am, &XB[buf][0][off >> 5][lane], PS);
+                const float inv = s_inv[buf][i][g], coef = s_coef[buf][i][g];
+                float u[4];
+                uint32_t pl[3];
+                if (nb == 1)
+                    encr_bucket<1>(acc, inv, coef, th, s_cent[g], u, pl);
+                else if (nb == 2)
+                    encr_bucket<2>(acc, inv, coef, th, s_cent[g], u, pl);
+                else
+                    encr_bucket<3>(acc, inv, coef, th, s_cent[g], u, pl);
+                // residual pieces in B-operand order
+                uint32_t pa[3], pb[3];
+                split3_pair(u[0], u[1], pa[0], pa[1], pa[2]);
+                split3_pair(u[2], u[3], pb[0], pb[1], pb[2]);
+                uint16_t *ub = reinterpret_cast<uint16_t *>(&UB[buf][0][0][0]) + u_elem;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float y = acc[r];
-                const float z = y * inv;
-                int idx = 0;
+                for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x2 *>(ub + p * PS * 8) = u32x2{pa[p], pb[p]};
+                float rr = 0.0f;
 #pragma unroll
-                for (int t = 0; t < 7; ++t) idx += z >= th[t] ? 1 : 0;
-                const float u = y - coef * s_cent[g][idx];
-                Uf[((wv * 64 + 16 * r + i) << 2) + q] = u;
-                rr += (double)u * (double)u;
-                pl01 |= ((uint32_t)(idx & 1) << r) | ((uint32_t)((idx >> 1) & 1) << (16 + r));
-                pl2 |= (uint32_t)((idx >> 2) & 1) << r;
+                for (int r = 0; r < 4; ++r) rr = fmaf(u[r], u[r], rr);
+                // nibbles of the four lane rows -> the 16 bits of this key's half-word
+                uint32_t pl01 = (pl[0] | (pl[1] << 16)) << (4 * q), pl2 = pl[2] << (4 * q);
+                pl01 = or_rows32(or_rows16(pl01));
+                rr = add_rows32(add_rows16(rr));
+                if (q == 0) s_rho[buf][wv][i] = rr;
+                if (nb > 2) pl2 = or_rows32(or_rows16(pl2));
+                if (q < nb) {
+                    const uint32_t vv = q == 0 ? (pl01 & 0xffffu) : (q == 1 ? (pl01 >> 16) : pl2);
+                    tw16[((tb * ENCS_WMAX + cw_word + q * wpp) * 16 + i) * 2 + cw_half] = (uint16_t)vv;
+                }
+            } else if (lane < 16) {
+                s_rho[buf][wv][lane] = 0.0f;
             }
-            pl01 <<= 4 * q;
-            pl2 <<= 4 * q;
-            pl01 |= __shfl_xor(pl01, 16, 64);
-            pl2 |= __shfl_xor(pl2, 16, 64);
-            rr += __shfl_xor(rr, 16, 64);
-            pl01 |= __shfl_xor(pl01, 32, 64);
-            pl2 |= __shfl_xor(pl2, 32, 64);
-            rr += __shfl_xor(rr, 32, 64);
-            if (q == 0) s_rho[wv][i] = rr;
-            // bit-plane p of these 16 coordinates is written by lane group p
-            if (q < nb) {
-                const uint32_t v = q == 0 ? (pl01 & 0xffffu) : (q == 1 ? (pl01 >> 16) : pl2);
-                tw16[((buf * ENCR_WMAX * 16) + (cw_word + q * wpp) * 16 + i) * 2 + cw_half] = (uint16_t)v;
+        } else {
+            // vector work first (it overlaps the rotation waves' MFMA chains), then the
+            // projection chain (it overlaps their bucketing)
+            // the tile after next: keys (loaded one step ago) into LDS, then the next load
+            const long ts = tr + grid;
+            if (ts < total_tiles) {
+                stage(ts, kq, buf ^ 1);
+                load_keys(ts + grid, kq);
             }
-        } else if (lane < 16) {
-            s_rho[wv][lane] = 0.0;
+            // tile tw is complete: its stored words, one coalesced block
+            if (tw >= 0 && st < a.W * 4)
+                reinterpret_cast<u32x4 *>(bits + (size_t)tw * a.W * 16)[st] =
+                    reinterpret_cast<const u32x4 *>(&TW[tb_w][0])[st];
+            if (tp >= 0 && tp < total_tiles) {
+                // residual norm rho = |u| (fp64 sum of the rotation waves' partial sums)
+                if (wv == ENCS_WAVES - 1 && lane < 16) {
+                    double s = 0.0;
+#pragma unroll
+                    for (int w = 0; w < ENCS_ROT; ++w) s += (double)s_rho[buf ^ 1][w][lane];
+                    rnorms[(size_t)tp * 16 + lane] = (float)sqrt(s);
+                }
+                // project tile tp's residual, add its sign words
+                if (prj_live) {
+                    const f32x4 acc = encs_mma_n<3>(nkb_p, am, &UB[buf ^ 1][0][0][lane], PS);
+                    uint32_t sg = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sg |= (acc[r] >= 0.0f ? 1u : 0u) << r;
+                    sg = or_rows32(or_rows16(sg << (4 * q)));
+                    if (q == 0) tw16[((tb_p * ENCS_WMAX + sw_word) * 16 + i) * 2 + sw_half] = (uint16_t)sg;
+                }
+            }
         }
         lds_barrier();
-        // the next tile's keys (loaded one tile ago) into the now free key buffer
-        const long Tn = T + grid;
-        if (Tn < total_tiles) {
-            stage(Tn, kq, buf ^ 1);
-            load_keys(Tn + grid, kq);
-        }
-        // stage 2: project the residual, keep the signs
-        if (prj_live) {
-            const f32x4 acc = encr_mma_n(nsp, rp, reinterpret_cast<const f32x4 *>(Uf) + lane);
-            uint32_t sg = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sg |= (acc[r] >= 0.0f ? 1u : 0u) << r;
-            sg <<= 4 * q;
-            sg |= __shfl_xor(sg, 16, 64);
-            sg |= __shfl_xor(sg, 32, 64);
-            if (q == 0) tw16[((buf * ENCR_WMAX * 16) + sw_word * 16 + i) * 2 + sw_half] = (uint16_t)sg;
-        }
-        // residual norm rho = |u| (fp64 sum of the waves' partial sums)
-        if (wv == ENCR_WAVES - 1 && lane < 16) {
-            double s = 0.0;
-#pragma unroll
-            for (int w = 0; w < ENCR_WAVES; ++w) s += s_rho[w][lane];
-            rnorms[(size_t)bank * n_pad + (size_t)tile * 16 + lane] = (float)sqrt(s);
-        }
-        lds_barrier();
-        // the tile's stored words: bits[bank][tile][W][16], one coalesced block
-        if (tid < a.W * 4)
-            reinterpret_cast<u32x4 *>(bits + (size_t)T * a.W * 16)[tid] =
-                reinterpret_cast<const u32x4 *>(&TW[buf][0])[tid];
     }
 }
 

@@ -296,21 +296,20 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     hipLaunchKernelGGL(enc_prep_proj_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p->proj, p->rot,
                        p->group_chan, a, sp);
     if ((rc = launch_status())) return rc;
-    // d, m <= 128 with aligned keys and words: the register-resident persistent encoder
-    const size_t kalign = dtype == TQ_F32 ? 16 : 8;
-    if (p->d <= ENCR_DMAX && p->m <= ENCR_DMAX && ((uintptr_t)keys % kalign) == 0 &&
-        ((uintptr_t)out->bits % 16) == 0) {
+    // d, m <= 128 with aligned words: the persistent bf16-split encoder
+    if (p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)out->bits % 16) == 0 &&
+        ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         const int64_t total = banks * n_tiles;
-        const dim3 pgrid((unsigned)std::min<int64_t>(total, 2 * (int64_t)std::max(cus, 1)));
+        const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
         if (dtype == TQ_F32)
-            hipLaunchKernelGGL(encode_regs_kernel<float>, pgrid, dim3(ENCR_WAVES * 64), 0, st, (const float *)keys,
-                               (long)n, (int)n_tiles, (long)total, p->rot, sp, p->group_chan, a, out->bits, out->norms,
+            hipLaunchKernelGGL(encode_split_kernel<float>, pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+                               (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits, out->norms,
                                out->rnorms);
         else
-            hipLaunchKernelGGL(encode_regs_kernel<uint16_t>, pgrid, dim3(ENCR_WAVES * 64), 0, st,
-                               (const uint16_t *)keys, (long)n, (int)n_tiles, (long)total, p->rot, sp, p->group_chan,
+            hipLaunchKernelGGL(encode_split_kernel<uint16_t>, pgrid, dim3(ENCS_WAVES * 64), 0, st,
+                               (const uint16_t *)keys, (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan,
                                a, out->bits, out->norms, out->rnorms);
         return launch_status();
     }

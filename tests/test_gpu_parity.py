@@ -205,6 +205,39 @@ def test_encode_bf16_and_f32_inputs_agree(tq):
         np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_encode_unaligned_keys(tq, dt):
+    """Keys at an address that is not a multiple of the vector-load width take the
+    tile-per-block encoder instead of the register-resident one: both meet the oracle,
+    and their outputs are compared word by word."""
+    import torch
+
+    cfg = workloads.CONFIGS["longctx"]
+    keys = workloads.keys(cfg, n=700, banks=[1, 2])
+    gpu, orc = both_params(cfg, 3)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    dense = torch.from_numpy(keys).cuda().to(tdt)
+    flat = torch.zeros(dense.numel() + 1, dtype=tdt, device="cuda")
+    flat[1:] = dense.reshape(-1)
+    shifted = flat[1:].view(dense.shape)
+    assert shifted.data_ptr() % 8 != 0
+    out = []
+    for src in (dense, shifted):
+        bank = tq.Bank(gpu, 2, 700)
+        tq.tq_encode(gpu, src, bank)
+        torch.cuda.synchronize()
+        out.append(download_bank(bank))
+    say(f"encode unaligned {dt}")
+    report = {}
+    for b in range(2):
+        ref = oracle.encode_trace(orc, keys[b])
+        check_encode((out[1][0][b], out[1][1][b], out[1][2][b]), ref, orc, 700, report)
+    diff = int((out[0][0] != out[1][0]).sum())
+    say("report", report, "words differing between the two encoders:", diff)
+    for b in range(2):  # the aligned call meets the oracle too
+        check_encode((out[0][0][b], out[0][1][b], out[0][2][b]), oracle.encode_trace(orc, keys[b]), orc, 700)
+
+
 def test_determinism(tq):
     import torch
 
