@@ -10,6 +10,7 @@
 
 #include "../../include/tq.h"
 #include "tq_encode.h"
+#include "tq_encode_gemm.h"
 #include "tq_score.h"
 #include "tq_topk.h"
 #include "tq_measure.h"
@@ -197,7 +198,35 @@ static PrepPlan prep_plan(int NF, int NCLS, int64_t banks, int32_t G) {
     return pl;
 }
 
-static size_t encode_ws(const tq_params *p) { return align256((size_t)p->m * p->d * 4); }
+// Encoder workspace: S' (fp32) always; for d or m above 128 also the bf16 pieces of R_g and
+// S', one residual chunk and the per-tile |u|^2 partial sums.
+struct EncWs {
+    size_t sp, r3[2], s3, U, rho, total;
+    int J;  // partial-sum slots per key row
+};
+static bool enc_large(const tq_params *p) { return p->d > ENCS_DMAX || p->m > ENCS_DMAX; }
+static EncWs enc_ws_layout(const tq_params *p, int64_t banks, int64_t n) {
+    EncWs w;
+    memset(&w, 0, sizeof(w));
+    size_t off = align256((size_t)p->m * p->d * 4);
+    if (enc_large(p)) {
+        for (int g = 0; g < p->n_groups; ++g) {
+            w.r3[g] = off;
+            off += align256((size_t)3 * p->group_dim[g] * p->group_dim[g] * 2);
+            w.J += 2 * ((p->group_dim[g] + EG_TILE - 1) / EG_TILE);
+        }
+        w.s3 = off;
+        off += align256((size_t)3 * p->m * p->d * 2);
+        const int64_t rows = banks * 16 * ((n + 15) / 16);
+        const int64_t urows = std::min<int64_t>(EG_CHUNK, (rows + EG_TILE - 1) / EG_TILE * EG_TILE);
+        w.U = off;
+        off += align256((size_t)urows * p->d * 4);
+        w.rho = off;
+        off += align256((size_t)w.J * EG_CHUNK * 4);
+    }
+    w.total = off;
+    return w;
+}
 
 // LDS-operand scorer / top-k: row tiles per work-group, query blocks, key chunks
 struct LdsPlan {
@@ -230,7 +259,7 @@ static size_t topk_part_bytes(int64_t banks, int32_t G, int kchunks, int32_t k) 
 
 extern "C" size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k) {
     if (check_params(p) || banks < 0 || n < 0) return 0;
-    if (op == TQ_OP_ENCODE) return encode_ws(p);
+    if (op == TQ_OP_ENCODE) return enc_ws_layout(p, banks, n).total;
     if (G < 1) return 0;
     size_t out = 0;
     const int rc = with_layout(p, [&](auto l) {
@@ -286,7 +315,8 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (banks < 0 || n < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
     if (!keys || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
-    if (!workspace || ws_bytes < encode_ws(p) || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    const EncWs ew = enc_ws_layout(p, banks, n);
+    if (!workspace || ws_bytes < ew.total || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
@@ -312,6 +342,45 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
                                (const uint16_t *)keys, (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan,
                                a, out->bits, out->norms, out->rnorms);
         return launch_status();
+    }
+    // larger keys with 16-byte aligned rows: the two-GEMM encoder, chunk by chunk
+    if (enc_large(p) && ((uintptr_t)keys % 16) == 0) {
+        char *ws = (char *)workspace;
+        for (int g = 0, goff = 0; g < p->n_groups; goff += p->group_dim[g] * p->group_dim[g], ++g) {
+            const long cnt = (long)p->group_dim[g] * p->group_dim[g];
+            hipLaunchKernelGGL(enc_split3_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st,
+                               p->rot + goff, cnt, (uint16_t *)(ws + ew.r3[g]));
+        }
+        hipLaunchKernelGGL(enc_split3_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, (const float *)sp,
+                           tot, (uint16_t *)(ws + ew.s3));
+        if ((rc = launch_status())) return rc;
+        const int64_t total = banks * n_tiles;
+        for (int64_t tc = 0; tc < total; tc += EG_CHUNK / 16) {
+            const int rows = (int)std::min<int64_t>(EG_CHUNK, (total - tc) * 16);
+            const int kblocks = (rows + EG_TILE - 1) / EG_TILE;
+            int jbase = 0;
+            for (int g = 0; g < p->n_groups; ++g) {
+                const int ntile = (p->group_dim[g] + EG_TILE - 1) / EG_TILE;
+                const dim3 grid((unsigned)(kblocks * ntile));
+                const uint16_t *r3 = (const uint16_t *)(ws + ew.r3[g]);
+                if (dtype == TQ_F32)
+                    hipLaunchKernelGGL(enc_gemm_rot_kernel<float>, grid, dim3(EG_THREADS), 0, st, (const float *)keys,
+                                       p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles, (long)n, jbase,
+                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, out->norms);
+                else
+                    hipLaunchKernelGGL(enc_gemm_rot_kernel<uint16_t>, grid, dim3(EG_THREADS), 0, st,
+                                       (const uint16_t *)keys, p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles,
+                                       (long)n, jbase, (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits,
+                                       out->norms);
+                jbase += 2 * ntile;
+            }
+            const dim3 pgrid((unsigned)(kblocks * ((p->m + EG_TILE - 1) / EG_TILE)));
+            hipLaunchKernelGGL(enc_gemm_prj_kernel, pgrid, dim3(EG_THREADS), 0, st, (const float *)(ws + ew.U),
+                               (const uint16_t *)(ws + ew.s3), a, (long)tc, rows, ew.J, (const float *)(ws + ew.rho),
+                               out->bits, out->rnorms);
+            if ((rc = launch_status())) return rc;
+        }
+        return TQ_OK;
     }
     const size_t smem = enc_smem_bytes(p->d, p->m);
     const dim3 grid((unsigned)(banks * n_tiles));

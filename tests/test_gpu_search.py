@@ -151,3 +151,54 @@ def test_topk_full_search_sampled(tq, bits):
         ref = oracle.score(orc, gb[0][0], gb[1][0], gb[2][0], n, qh[0, qi:qi + 1])
         same = check_topk(vals.cpu().numpy()[0, qi:qi + 1], idx.cpu().numpy()[0, qi:qi + 1], ref, k, f"query {qi}")
         say(f"   query {qi}: overlap with the oracle's top-{k} {same:.2f}")
+
+
+# ------------------------------------------------------------------------------------------
+# encoder for keys above 128 dimensions (tiled two-GEMM path): partial tiles, two channel
+# groups with a channel permutation, bf16 and fp32 keys, several residual chunks
+# ------------------------------------------------------------------------------------------
+
+def _large_cfg(d, m, groups, key_dtype, cfg_id):
+    import dataclasses
+
+    base = workloads.CONFIGS["longctx"] if groups else workloads.CONFIGS["decode8b"]
+    extra = dict(outliers=groups[0][0], groups=groups) if groups else {}
+    return dataclasses.replace(base, d=d, m=m, key_dtype=key_dtype, cfg_id=cfg_id, **extra)
+
+
+def _encode_vs_oracle(tq, cfg, bits, keys):
+    import torch
+
+    gpu, orc = both_params(cfg, bits)
+    banks, n = keys.shape[0], keys.shape[1]
+    bank = tq.Bank(gpu, banks, n)
+    t = torch.from_numpy(np.ascontiguousarray(keys)).cuda()
+    tq.tq_encode(gpu, t.to(torch.bfloat16) if cfg.key_dtype == "bf16" else t, bank)
+    torch.cuda.synchronize()
+    gb = download_bank(bank)
+    rep = {}
+    for b in range(banks):
+        check_encode((gb[0][b], gb[1][b], gb[2][b]), oracle.encode_trace(orc, keys[b]), orc, n, rep)
+    return rep
+
+
+@pytest.mark.parametrize("d,m,groups,dt", [
+    (256, 160, ((64, 3), (192, 2)), "bf16"),  # two groups, permuted channels, partial row tile
+    (160, 288, None, "f32"),                  # partial coordinate and row tiles, fp32 keys
+    (256, 128, ((96, 2), (160, 3)), "f32"),   # d above 128 with m at 128
+    (128, 256, None, "bf16"),                 # m above 128 with d at 128
+])
+def test_encode_large_keys(tq, d, m, groups, dt):
+    cfg = _large_cfg(d, m, groups, dt, 60 + d // 32 + m // 32)
+    keys = workloads.keys(cfg, n=1500, banks=[0, 1])
+    say(f"encode large keys d={d} m={m} groups={groups} {dt}")
+    bits = 3 if groups is None else cfg.bits[0]
+    say("   report", _encode_vs_oracle(tq, cfg, bits, keys))
+
+
+def test_encode_large_keys_several_chunks(tq):
+    """More key rows than one residual chunk (32768): the chunk boundary falls inside a bank."""
+    cfg = _large_cfg(256, 256, None, "bf16", 71)
+    keys = workloads.keys(cfg, n=11111, banks=[0, 1, 2])
+    say("encode large keys, 3 x 11111 keys (two residual chunks)")
+    say("   report", _encode_vs_oracle(tq, cfg, 3, keys))
