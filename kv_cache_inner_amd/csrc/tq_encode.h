@@ -18,6 +18,8 @@
 //   4. bit-planes and sign words packed from LDS, written as the bank tile
 //      [W][16] (one coalesced store per word row).
 #pragma once
+#include <float.h>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -544,13 +546,21 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     contig = contig && (xo[0] & 3) == 0;
     const int key_off = ik * D + 4 * cq;
 
+    // (bank, tile) of the next key load; loads go to tiles blockIdx.x + k * grid, k = 0, 1, ...
+    int l_bank = (int)blockIdx.x / n_tiles, l_tile = (int)blockIdx.x - l_bank * n_tiles;
+    const int step_banks = grid / n_tiles, step_tiles = grid - step_banks * n_tiles;
     auto load_keys = [&](long T, KeyQuad<KT> &kq) {
         kq.zero();
         if (T < total_tiles) {
-            const int bank = (int)T / n_tiles;
-            const long key0 = (long)((int)T - bank * n_tiles) * 16;
-            const KT *tile_keys = keys + ((size_t)bank * n + key0) * D;  // wave-uniform
+            const long key0 = (long)l_tile * 16;
+            const KT *tile_keys = keys + ((size_t)l_bank * n + key0) * D;  // wave-uniform
             if (cq_live && key0 + ik < n) kq.load(tile_keys + key_off);
+        }
+        l_bank += step_banks;
+        l_tile += step_tiles;
+        if (l_tile >= n_tiles) {
+            l_tile -= n_tiles;
+            ++l_bank;
         }
     };
     // keys -> LDS operand order (pieces for fp32 keys); per-group norms
@@ -599,8 +609,18 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
         s0 = sum_half_wave(s0);
         if (cq < ng) {
             const float s = cq ? s1 : s0;
-            const float nu = sqrtf(s);
-            s_inv[buf][ik][cq] = s > 0.0f ? (cq ? sqrt_d1 : sqrt_d0) / nu : 0.0f;
+            // |x| = s rsq(s) and sqrt(d)/|x| = sqrt(d) rsq(s) (v_rsq_f32, within 1 ulp) for a
+            // normal s; the correctly rounded forms for zero and subnormal sums
+            float nu, inv;
+            if (s >= FLT_MIN) {
+                const float rs = __builtin_amdgcn_rsqf(s);
+                nu = s * rs;
+                inv = (cq ? sqrt_d1 : sqrt_d0) * rs;
+            } else {
+                nu = sqrtf(s);
+                inv = s > 0.0f ? (cq ? sqrt_d1 : sqrt_d0) / nu : 0.0f;
+            }
+            s_inv[buf][ik][cq] = inv;
             s_coef[buf][ik][cq] = nu * (cq ? inv_sqrt_d1 : inv_sqrt_d0);
             norms[((size_t)T * 16 + ik) * ng + cq] = nu;  // bank * n_pad + key == 16 T + ik
         }
