@@ -8,7 +8,8 @@ sketch, m = 128). Value = estimated inner products per second.
 
 The same run also times the encoder over all 32 layers (keys/s), the b = 4
 variant of the sweep, the fp32 unquantized-keys logits kernel on the same
-shapes, and the CPU oracle on a bounded sample (rank 0). Prints ONE JSON line.
+shapes, the long-context and vector-search workloads, streaming appends, and
+the CPU oracle on a bounded sample (rank 0). Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--quick]
 """
@@ -28,6 +29,26 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def encode_rates(keys, ms, d, m, groups, bf16_keys):
+    """Encoder rates: algorithmic fp32 contraction flops (rotation 2 d_g^2 per group,
+    projection 2 m d per key) and the bf16 matrix flops actually issued (every fp32 operand
+    is three exact bf16 pieces; bf16 keys are one piece: rotation 3 products, otherwise 6;
+    projection 6)."""
+    rot = sum(2 * dg * dg for dg in groups)
+    prj = 2 * m * d
+    issued = rot * (3 if bf16_keys else 6) + prj * 6
+    sec = ms * 1e-3
+    return {
+        "keys_per_s": keys / sec,
+        "ms": ms,
+        "fp32_equivalent_tflops": keys * (rot + prj) / sec / 1e12,
+        "fp32_equivalent_frac_of_fp32_mfma_peak": keys * (rot + prj) / sec / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "bf16_mfma_issued_tflops": keys * issued / sec / 1e12,
+        "bf16_mfma_frac": keys * issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+    }
 METRIC = "packed-key inner products/sec + HBM GB/s (% peak), d=128 b=3, 32K ctx decode"
 
 
@@ -269,12 +290,47 @@ def longctx_extra(tq, device):
         "workload": "longctx: 8 banks x 131072 bf16 keys, groups (32 ch, 2-bit codebook) + (96 ch, 1-bit), "
                     "one 128-row sign sketch, G=4",
         "bytes_per_key": int(bpk),
-        "encode_keys_per_s": keys_n / (enc_ms * 1e-3),
-        "encode_ms": enc_ms,
+        "encode": encode_rates(keys_n, enc_ms, cfg.d, cfg.m, [g[0] for g in cfg.groups], True),
         "score_pairs_per_s": keys_n * cfg.G / (sc_ms * 1e-3),
         "score_ms": sc_ms,
         "score_gbps": keys_n * (bpk + 4 * cfg.G) / (sc_ms * 1e-3) / 1e9,
     }
+
+
+def append_extra(tq, device):
+    """Streaming append on the 8B-class shapes: one new key per bank (64 banks, capacity
+    32768 + 16 slots) per layer call, as in a decode step, and 16 keys per bank per call."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    prm = params_for(tq, cfg, 3, device)
+    n_cap = cfg.tokens + 16
+    banks = [tq.Bank(prm, cfg.banks, n_cap, device) for _ in range(2)]
+    out = {"workload": "decode8b: 64 banks of 32784 slots, b=3; keys appended at slot 32768 onwards"}
+    for count in (1, 16):
+        keys = torch.randn(cfg.banks, count, cfg.d, device=device).to(torch.bfloat16)
+        pos = torch.full((cfg.banks,), cfg.tokens, dtype=torch.int32, device=device)
+        ws = torch.empty(prm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, count), dtype=torch.uint8, device=device)
+        res = {}
+        for prepared in (False, True):
+            for i in range(4):
+                tq.tq_encode_append(prm, keys, banks[i % 2], pos, workspace=ws, prepared=prepared and i > 0)
+            calls = 64
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(calls):
+                tq.tq_encode_append(prm, keys, banks[i % 2], pos, workspace=ws, prepared=prepared)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / calls
+            res["prepared" if prepared else "with_projection_fold"] = {
+                "us_per_call": us, "keys_per_s": cfg.banks * count / (us * 1e-6),
+                "us_per_decode_step_32_layers": 32 * us}
+        out[f"count{count}"] = res
+    del banks
+    torch.cuda.empty_cache()
+    return out
 
 
 def search_extra(tq, device):
@@ -314,8 +370,7 @@ def search_extra(tq, device):
         recall = (idx[0].long()[:, :, None] == exact[:, None, :]).any(dim=2).float().mean().item()
         pairs = cfg.tokens * cfg.G
         out[f"b{bits}"] = {
-            "encode_keys_per_s": cfg.tokens / (enc_ms * 1e-3),
-            "encode_ms": enc_ms,
+            "encode": encode_rates(cfg.tokens, enc_ms, cfg.d, cfg.m, [cfg.d], False),
             "topk_ms": tk_ms,
             "topk_pairs_per_s": pairs / (tk_ms * 1e-3),
             "topk_tflops_algorithmic": pairs * 2 * (cfg.d + cfg.m) / (tk_ms * 1e-3) / 1e12,
@@ -411,12 +466,7 @@ def main():
             "launches": len(kern_ms) * L,
         },
         "hbm_copy_ceiling": copy_ceiling(tq, device, bytes_per_launch),
-        "encode": {
-            "keys_per_s": keys_total / (enc_ms * 1e-3),
-            "ms_total": enc_ms,
-            "tflops": keys_total * 2 * cfg.d * (cfg.d + cfg.m) / (enc_ms * 1e-3) / 1e12,
-            "mfma_fp32_frac": keys_total * 2 * cfg.d * (cfg.d + cfg.m) / (enc_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
-        },
+        "encode": dict(encode_rates(keys_total, enc_ms, cfg.d, cfg.m, [cfg.d], True), layers=L),
     }
     del sw3
     torch.cuda.empty_cache()
@@ -463,6 +513,8 @@ def main():
         torch.cuda.empty_cache()
         log("vector search top-10")
         out["search"] = search_extra(tq, device)
+        log("streaming append")
+        out["append"] = append_extra(tq, device)
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

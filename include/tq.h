@@ -60,6 +60,11 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 typedef enum { TQ_OP_ENCODE = 0, TQ_OP_SCORE = 1, TQ_OP_TOPK = 2 } tq_op;
 
+/* tq_encode_append flags. TQ_APPEND_PREPARED: the workspace already holds this call's
+ * folded projection S' = S P_chan blockdiag(R_g)^T, written by an earlier tq_encode or
+ * tq_encode_append with the same parameters into the same workspace; it is not formed again. */
+enum { TQ_APPEND_PREPARED = 1 };
+
 /* Parameters of one encoding. Dimensions and the codebooks are host values;
  * the matrices are (device) pointers read by the kernels.
  *   d            key dimension; d = group_dim[0] (+ group_dim[1])
@@ -123,6 +128,22 @@ size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, 
  * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, ...). */
 int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t n, const tq_bank *out,
               void *workspace, size_t ws_bytes, void *stream);
+
+/* Streaming append (online encoding: the quantiser is data-oblivious, so a new key is
+ * encoded on its own, with nothing recomputed for the keys already stored; turboquant-pytorch
+ * write-up, two-stage algorithm section). Encodes `count` new keys per bank, keys (device)
+ * [banks][count][d] of dtype TQ_F32 or TQ_BF16, into slots pos[b] .. pos[b] + count - 1 of
+ * bank b of `out`, whose arrays are sized by tq_bank_layout for n_cap slots per bank.
+ * pos (device) int32[banks]. A key whose slot falls outside [0, n_cap_pad) (n_cap_pad =
+ * 16 * ceil(n_cap / 16)) is skipped; no other slot is written. Slots are encoded as
+ * tq_encode encodes them (up to the decision band of the fp32-level contractions). Uses
+ * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, p, banks, count, ...) bytes;
+ * flags: 0 or TQ_APPEND_PREPARED (any other bit: TQ_ERR_ARG). Scoring a bank filled this way
+ * uses n = n_cap: slots never written hold whatever the arrays held. TQ_ERR_UNSUPPORTED when
+ * the per-tile LDS footprint (16 keys x (8 d + 2 (d + m)) bytes) exceeds 150 KiB. */
+int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                     const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
+                     size_t ws_bytes, void *stream);
 
 /* Query preparation (per query: R_g q_g and S q, once, as the estimator's
  * operands; same write-up, usage example: the query stays at full precision).

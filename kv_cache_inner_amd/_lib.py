@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libtq.so")
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_DEVICE, TQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
 TQ_F32, TQ_BF16 = 0, 1
 TQ_OP_ENCODE, TQ_OP_SCORE, TQ_OP_TOPK = 0, 1, 2
+TQ_APPEND_PREPARED = 1
 
 
 class TQError(RuntimeError):
@@ -41,7 +42,7 @@ class tq_bank(ctypes.Structure):
 
 
 EXPORTS = ["tq_make_codebook", "tq_make_rotation", "tq_bank_layout", "tq_workspace_bytes", "tq_encode",
-           "tq_prepare_queries", "tq_score_prepared", "tq_score", "tq_topk", "tq_fp32_logits", "tq_copy",
+           "tq_encode_append", "tq_prepare_queries", "tq_score_prepared", "tq_score", "tq_topk", "tq_fp32_logits", "tq_copy",
            "tq_status_string"]
 
 
@@ -58,6 +59,7 @@ def _load():
         "tq_bank_layout": (ctypes.c_int, [P, i64, vp, vp, vp]),
         "tq_workspace_bytes": (sz, [ctypes.c_int, P, i64, i64, i32, i32]),
         "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, B, vp, sz, vp]),
+        "tq_encode_append": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, vp, i64, B, ctypes.c_int, vp, sz, vp]),
         "tq_prepare_queries": (ctypes.c_int, [P, vp, i64, i32, vp, sz, vp]),
         "tq_score_prepared": (ctypes.c_int, [P, B, i64, i64, i32, vp, vp, vp]),
         "tq_score": (ctypes.c_int, [P, B, i64, i64, vp, i32, vp, vp, sz, vp]),
@@ -214,6 +216,25 @@ def tq_encode(params: Params, keys, bank: Bank, workspace=None, stream=None):
     ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
     _check("tq_encode", _lib.tq_encode(params.ref, keys.data_ptr(), dtype, banks, n, bank.ref, ws.data_ptr(),
                                        ws.numel(), _stream(stream)))
+    return bank
+
+
+def tq_encode_append(params: Params, keys, bank: Bank, pos, workspace=None, prepared=False, stream=None):
+    """Encodes keys [banks][count][d] into slots pos[b] .. pos[b] + count - 1 of each bank of
+    `bank` (allocated for bank.n slots per bank); pos: device int32 tensor [banks].
+    prepared=True: `workspace` already holds S' from an earlier encode with these params."""
+    import torch
+
+    assert keys.is_contiguous() and keys.dim() == 3 and keys.shape[2] == params.d
+    assert keys.dtype in (torch.bfloat16, torch.float32)
+    assert pos.dtype == torch.int32 and pos.is_contiguous() and pos.numel() == keys.shape[0] == bank.banks
+    dtype = TQ_BF16 if keys.dtype == torch.bfloat16 else TQ_F32
+    banks, count = keys.shape[0], keys.shape[1]
+    ws_bytes = params.workspace_bytes(TQ_OP_ENCODE, banks, count)
+    ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
+    _check("tq_encode_append", _lib.tq_encode_append(params.ref, keys.data_ptr(), dtype, banks, count, pos.data_ptr(),
+                                                     bank.n, bank.ref, TQ_APPEND_PREPARED if prepared else 0,
+                                                     ws.data_ptr(), ws.numel(), _stream(stream)))
     return bank
 
 

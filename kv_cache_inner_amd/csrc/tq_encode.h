@@ -35,22 +35,28 @@ struct EncArgs {
     double sqrt_d[2];
 };
 
-// S'[i][pos] for pos = goff[g] + j: sum_k S[i][chan[goff[g]+k]] * R_g[j][k]  (fp64 sums)
+// S'[i][pos] for pos = goff[g] + j: sum_k S[i][chan[goff[g]+k]] * R_g[j][k] (fp64 sums in
+// ascending k). One work-group per row i of S (its permuted row staged in LDS), one thread
+// per output column.
 __global__ __launch_bounds__(256) void enc_prep_proj_kernel(const float *__restrict__ S, const float *__restrict__ rot,
                                                             const int *__restrict__ chan, EncArgs a,
                                                             float *__restrict__ sp) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)a.m * a.d) return;
-    const int i = (int)(idx / a.d), pos = (int)(idx % a.d);
+    __shared__ double s_row[1024];
+    const long i = blockIdx.y;
+    for (int pos = threadIdx.x; pos < a.d; pos += blockDim.x) {
+        const int c = chan ? chan[pos] : pos;
+        s_row[pos] = (double)S[i * a.d + ((unsigned)c < (unsigned)a.d ? c : 0)];
+    }
+    __syncthreads();
+    const int pos = blockIdx.x * blockDim.x + threadIdx.x;
+    if (pos >= a.d) return;
     const int g = (a.ng > 1 && pos >= a.gdim[0]) ? 1 : 0;
     const int dg = a.gdim[g], off = a.goff[g], j = pos - off;
     const float *R = rot + (g ? (long)a.gdim[0] * a.gdim[0] : 0) + (long)j * dg;
     double s = 0.0;
-    for (int k = 0; k < dg; ++k) {
-        const int c = chan ? chan[off + k] : off + k;
-        s += (double)S[(long)i * a.d + c] * (double)R[k];
-    }
-    sp[(long)i * a.d + pos] = (float)s;
+#pragma unroll 8
+    for (int k = 0; k < dg; ++k) s += s_row[off + k] * (double)R[k];
+    sp[i * a.d + pos] = (float)s;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -92,12 +98,21 @@ inline size_t enc_smem_bytes(int d, int m) {
     return (size_t)2 * ENC_KEYS * (d + 2) * 4 + (size_t)ENC_KEYS * d + (size_t)ENC_KEYS * m;
 }
 
+// Where the keys of a call are stored. Default (pos == nullptr): key k of bank b at slot k
+// of banks of n_tiles tiles, the padding slots of the last tile included. Appending: key k
+// at slot pos[b] + k of banks of cap_tiles tiles, only keys k < n whose slot is in
+// [0, 16 cap_tiles); no other slot is written.
+struct EncSlots {
+    const int32_t *pos;
+    int cap_tiles;
+};
+
 template <typename KT>
 __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys, long n, int n_tiles,
                                                      const float *__restrict__ rot, const float *__restrict__ sp,
                                                      const int *__restrict__ chan, EncArgs a,
                                                      uint32_t *__restrict__ bits, float *__restrict__ norms,
-                                                     float *__restrict__ rnorms) {
+                                                     float *__restrict__ rnorms, EncSlots slots) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float s_inv[ENC_KEYS][2], s_coef[ENC_KEYS][2], s_cent[2][16];
     const int d = a.d, m = a.m, ld = d + 2;
@@ -111,6 +126,14 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const long n_pad = (long)n_tiles * ENC_KEYS;
     const long key0 = (long)tile * ENC_KEYS;
+    // output slot of key key0 + i within its bank (-1: not stored), and the bank's slot count
+    const long out_pad = slots.pos ? (long)slots.cap_tiles * ENC_KEYS : n_pad;
+    const long slot_base = slots.pos ? (long)slots.pos[bank] + key0 : key0;
+    auto slot_of = [&](int i) -> long {
+        const long sl = slot_base + i;
+        if (!slots.pos) return sl;
+        return (key0 + i < n && sl >= 0 && sl < out_pad) ? sl : -1;
+    };
 
     if (tid < 32) s_cent[tid >> 4][tid & 15] = a.cent[tid >> 4][tid & 15];
     // 1. keys -> LDS in group order
@@ -138,7 +161,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
                 const float nu_s = (float)nu;
                 s_inv[i][g] = nu > 0.0 ? (float)(a.sqrt_d[g] / nu) : 0.0f;
                 s_coef[i][g] = (float)((double)nu_s / a.sqrt_d[g]);
-                norms[((size_t)bank * n_pad + key0 + i) * a.ng + g] = nu_s;
+                const long sl = slot_of(i);
+                if (sl >= 0) norms[((size_t)bank * out_pad + sl) * a.ng + g] = nu_s;
             }
         }
     }
@@ -191,7 +215,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
             s += v * v;
         }
         s = wave_sum_f64(s);
-        if (lane == 0) rnorms[(size_t)bank * n_pad + key0 + i] = (float)sqrt(s);
+        const long sl = slot_of(i);
+        if (lane == 0 && sl >= 0) rnorms[(size_t)bank * out_pad + sl] = (float)sqrt(s);
     }
 
     // 4. stage 2 on MFMA: P = U S'^T, sign = [P >= 0]
@@ -220,8 +245,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
     }
     __syncthreads();
 
-    // 5. pack the tile: word w of key i -> bits[bank][tile][w][i]
-    uint32_t *tb = bits + ((size_t)bank * n_tiles + tile) * (size_t)a.W * ENC_KEYS;
+    // 5. pack the tile: word w of the key in slot sl -> bits[bank][sl / 16][w][sl % 16]
+    uint32_t *bb = bits + (size_t)bank * (out_pad / ENC_KEYS) * a.W * ENC_KEYS;
     for (int item = tid; item < a.W * ENC_KEYS; item += 256) {
         const int w = item / ENC_KEYS, i = item % ENC_KEYS;
         uint32_t word;
@@ -233,7 +258,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
         } else {
             word = pack_plane(SG + i * m + 32 * (w - a.sword), 0);
         }
-        tb[item] = word;
+        const long sl = slot_of(i);
+        if (sl >= 0) bb[((size_t)(sl / ENC_KEYS) * a.W + w) * ENC_KEYS + sl % ENC_KEYS] = word;
     }
 }
 
@@ -470,7 +496,7 @@ template <typename KT>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
-    float *__restrict__ norms, float *__restrict__ rnorms) {
+    float *__restrict__ norms, float *__restrict__ rnorms, EncSlots slots) {
     constexpr int XP = sizeof(KT) == 2 ? 1 : 3;  // key pieces: bf16 keys are exact in one
     constexpr int PS = 4 * 64;                     // piece stride of the operand buffers (u32x4)
     __shared__ __align__(16) u32x4 XB[2][XP][4][64];
@@ -545,6 +571,15 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     }
     contig = contig && (xo[0] & 3) == 0;
     const int key_off = ik * D + 4 * cq;
+    // flat output slot (bank * slots per bank + slot) of key i of input tile T, or -1 when the
+    // key is not stored (appending: past the input keys, or outside the bank)
+    const long out_pad = slots.pos ? (long)slots.cap_tiles * 16 : 0;
+    auto out_slot = [&](long T, int ki) -> long {
+        if (!slots.pos) return T * 16 + ki;
+        const long bank = T / n_tiles, k = (T - bank * n_tiles) * 16 + ki;
+        const long sl = (long)slots.pos[bank] + k;
+        return (k < n && sl >= 0 && sl < out_pad) ? bank * out_pad + sl : -1;
+    };
 
     // (bank, tile) of the next key load; loads go to tiles blockIdx.x + k * grid, k = 0, 1, ...
     int l_bank = (int)blockIdx.x / n_tiles, l_tile = (int)blockIdx.x - l_bank * n_tiles;
@@ -622,7 +657,8 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
             }
             s_inv[buf][ik][cq] = inv;
             s_coef[buf][ik][cq] = nu * (cq ? inv_sqrt_d1 : inv_sqrt_d0);
-            norms[((size_t)T * 16 + ik) * ng + cq] = nu;  // bank * n_pad + key == 16 T + ik
+            const long fs = out_slot(T, ik);
+            if (fs >= 0) norms[(size_t)fs * ng + cq] = nu;
         }
     };
 
@@ -687,16 +723,21 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
                 load_keys(ts + grid, kq);
             }
             // tile tw is complete: its stored words, one coalesced block
-            if (tw >= 0 && st < a.W * 4)
+            if (tw >= 0 && !slots.pos && st < a.W * 4)
                 reinterpret_cast<u32x4 *>(bits + (size_t)tw * a.W * 16)[st] =
                     reinterpret_cast<const u32x4 *>(&TW[tb_w][0])[st];
+            if (tw >= 0 && slots.pos && st < a.W * 16) {  // appending: each key to its slot
+                const long fs = out_slot(tw, st & 15);
+                if (fs >= 0) bits[((size_t)(fs >> 4) * a.W + (st >> 4)) * 16 + (fs & 15)] = TW[tb_w][st];
+            }
             if (tp >= 0 && tp < total_tiles) {
                 // residual norm rho = |u| (fp64 sum of the rotation waves' partial sums)
                 if (wv == ENCS_WAVES - 1 && lane < 16) {
                     double s = 0.0;
 #pragma unroll
                     for (int w = 0; w < ENCS_ROT; ++w) s += (double)s_rho[buf ^ 1][w][lane];
-                    rnorms[(size_t)tp * 16 + lane] = (float)sqrt(s);
+                    const long fs = out_slot(tp, lane);
+                    if (fs >= 0) rnorms[fs] = (float)sqrt(s);
                 }
                 // project tile tp's residual, add its sign words
                 if (prj_live) {

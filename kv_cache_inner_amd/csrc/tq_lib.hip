@@ -308,6 +308,12 @@ static EncArgs enc_args(const tq_params *p) {
     return a;
 }
 
+static void launch_prep_proj(const tq_params *p, const EncArgs &a, float *sp, hipStream_t st) {
+    const int bx = p->d <= 64 ? 64 : (p->d <= 128 ? 128 : 256);
+    hipLaunchKernelGGL(enc_prep_proj_kernel, dim3((unsigned)((p->d + bx - 1) / bx), (unsigned)p->m), dim3(bx), 0, st,
+                       p->proj, p->rot, p->group_chan, a, sp);
+}
+
 extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t n, const tq_bank *out,
                          void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(p);
@@ -323,8 +329,7 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     const EncArgs a = enc_args(p);
     float *sp = (float *)workspace;
     const long tot = (long)p->m * p->d;
-    hipLaunchKernelGGL(enc_prep_proj_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p->proj, p->rot,
-                       p->group_chan, a, sp);
+    launch_prep_proj(p, a, sp, st);
     if ((rc = launch_status())) return rc;
     // d, m <= 128 with aligned words: the persistent bf16-split encoder
     if (p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)out->bits % 16) == 0 &&
@@ -336,11 +341,11 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
         if (dtype == TQ_F32)
             hipLaunchKernelGGL(encode_split_kernel<float>, pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
                                (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits, out->norms,
-                               out->rnorms);
+                               out->rnorms, EncSlots{nullptr, 0});
         else
             hipLaunchKernelGGL(encode_split_kernel<uint16_t>, pgrid, dim3(ENCS_WAVES * 64), 0, st,
                                (const uint16_t *)keys, (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan,
-                               a, out->bits, out->norms, out->rnorms);
+                               a, out->bits, out->norms, out->rnorms, EncSlots{nullptr, 0});
         return launch_status();
     }
     // larger keys with 16-byte aligned rows: the two-GEMM encoder, chunk by chunk
@@ -383,15 +388,68 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
         return TQ_OK;
     }
     const size_t smem = enc_smem_bytes(p->d, p->m);
+    if (smem > 150 * 1024) return TQ_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)(banks * n_tiles));
     if (dtype == TQ_F32) {
         (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)n, (int)n_tiles,
-                           p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms);
+                           p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, EncSlots{nullptr, 0});
     } else {
         (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)n,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms);
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms,
+                           EncSlots{nullptr, 0});
+    }
+    return launch_status();
+}
+
+extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                                const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || count < 0 || n_cap < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
+    if (flags & ~TQ_APPEND_PREPARED) return TQ_ERR_ARG;
+    if (banks == 0 || count == 0 || n_cap == 0) return TQ_OK;
+    if (!keys || !pos || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
+    if (!workspace || ws_bytes < enc_ws_layout(p, banks, count).total || ((uintptr_t)workspace & 255))
+        return TQ_ERR_WORKSPACE;
+    const int64_t n_tiles = (count + 15) / 16, cap_tiles = (n_cap + 15) / 16;
+    if (banks * n_tiles > INT32_MAX || cap_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+    const size_t smem = enc_smem_bytes(p->d, p->m);
+    if (smem > 150 * 1024) return TQ_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    const EncArgs a = enc_args(p);
+    float *sp = (float *)workspace;
+    if (!(flags & TQ_APPEND_PREPARED)) {
+        launch_prep_proj(p, a, sp, st);
+        if ((rc = launch_status())) return rc;
+    }
+    const EncSlots slots{pos, (int)cap_tiles};
+    if (p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0) {
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const int64_t total = banks * n_tiles;
+        const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
+        if (dtype == TQ_F32)
+            hipLaunchKernelGGL(encode_split_kernel<float>, pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+                               (long)count, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits,
+                               out->norms, out->rnorms, slots);
+        else
+            hipLaunchKernelGGL(encode_split_kernel<uint16_t>, pgrid, dim3(ENCS_WAVES * 64), 0, st,
+                               (const uint16_t *)keys, (long)count, (int)n_tiles, (int)total, p->rot, sp,
+                               p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
+        return launch_status();
+    }
+    const dim3 grid((unsigned)(banks * n_tiles));
+    if (dtype == TQ_F32) {
+        (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)count,
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
+    } else {
+        (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)count,
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
     }
     return launch_status();
 }

@@ -339,3 +339,69 @@ def test_longctx_full_size_sampled(tq):
         qi = g.integers(0, cfg.G, len(kk))
         ref = oracle.score_pairs(orc, gb[0][b], gb[1][b], gb[2][b], qh[b], qi, kk)
         check_scores(scores[b, qi, kk], ref, f"bank {b}")
+
+
+# ------------------------------------------------------------------------------------------
+# streaming append: keys encoded into chosen slots of preallocated banks
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_encode_append_slots(tq, unaligned):
+    """Appends in three calls at different per-bank positions (not multiples of 16), one of
+    them running past the capacity; appended slots match the oracle's encoding of their keys
+    and every other slot keeps its previous bytes. Unaligned key rows take the
+    tile-per-block encoder, aligned ones the persistent one."""
+    import torch
+
+    cfg = workloads.CONFIGS["longctx"]
+    gpu, orc = both_params(cfg, 3)
+    n_cap, banks = 100, 2
+    keys = workloads.keys(cfg, n=64, banks=[2, 3])
+    bank = tq.Bank(gpu, banks, n_cap)
+    bank.bits.fill_(0x5A5A5A5A)
+    bank.norms.fill_(-1.0)
+    bank.rnorms.fill_(-2.0)
+    start = np.array([0, 5], np.int64)
+    calls = [(0, 37), (37, 38), (38, 64)]  # [key range) per call
+    filled = {0: {}, 1: {}}  # bank -> slot -> key index
+    ws = torch.empty(gpu.workspace_bytes(tq.TQ_OP_ENCODE, banks, 64), dtype=torch.uint8, device="cuda")
+    for k0, k1 in calls:
+        pos = start + k0
+        if k0 == 38:
+            pos[1] = n_cap - 7  # bank 1: only 7 of these 26 keys fit (the rest are skipped)
+        kk = torch.from_numpy(np.ascontiguousarray(keys[:, k0:k1])).cuda().to(torch.bfloat16)
+        if unaligned:  # the same values at an address that is not a multiple of 8 bytes
+            flat = torch.zeros(kk.numel() + 1, dtype=torch.bfloat16, device="cuda")
+            flat[1:] = kk.reshape(-1)
+            kk = flat[1:].view(kk.shape)
+        say(f"append keys [{k0}, {k1}) at slots {pos.tolist()}")
+        # the first call forms S' in the workspace, the later ones reuse it
+        tq.tq_encode_append(gpu, kk, bank, torch.from_numpy(pos.astype(np.int32)).cuda(), workspace=ws,
+                            prepared=k0 > 0)
+        for b in range(banks):
+            for j in range(k1 - k0):
+                sl = int(pos[b]) + j
+                if 0 <= sl < bank.n_pad:
+                    filled[b][sl] = k0 + j
+    torch.cuda.synchronize()
+    gb, gn, gr = download_bank(bank)
+    report = {}
+    for b in range(banks):
+        slots = np.array(sorted(filled[b]), np.int64)
+        kidx = np.array([filled[b][s] for s in slots], np.int64)
+        # the appended records, gathered into a fresh tile array in slot order
+        W = gb.shape[2]
+        words = gb[b].transpose(0, 2, 1).reshape(-1, W)[slots]
+        n_new = len(slots)
+        pad = (-n_new) % 16
+        ref = oracle.encode_trace(orc, keys[b][kidx])
+        # the gathered array's padding rows are the oracle's (zero-vector records)
+        ref_rows = ref[0].transpose(0, 2, 1).reshape(-1, W)
+        tiles = np.concatenate([words, ref_rows[n_new:]]).reshape(-1, 16, W).transpose(0, 2, 1)
+        check_encode((tiles, np.concatenate([gn[b][slots], np.zeros((pad, gn.shape[2]), np.float32)]),
+                      np.concatenate([gr[b][slots], np.zeros(pad, np.float32)])), ref, orc, n_new, report)
+        untouched = np.setdiff1d(np.arange(bank.n_pad), slots)
+        assert (gb[b].transpose(0, 2, 1).reshape(-1, W)[untouched] == 0x5A5A5A5A).all()
+        assert (gn[b][untouched] == -1.0).all() and (gr[b][untouched] == -2.0).all()
+    assert len(filled[1]) == 37 + 1 + 7 + (bank.n_pad - n_cap)
+    say("report", report)

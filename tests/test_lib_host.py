@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol(tq):
     names = _declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = ctypes.CDLL(tq.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -178,6 +178,18 @@ def test_argument_validation_returns_before_any_launch(tq):
                      None) == tq.TQ_ERR_WORKSPACE
     assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4001, 1 << 20,
                      None) == tq.TQ_ERR_WORKSPACE
+    # append: null keys or positions, negative sizes, bad dtype, small or misaligned workspace
+    A = L.tq_encode_append
+    assert A(good.ref, None, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 0, 1, 1, None, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 0, 1, -1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, -5, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 3, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(nullbank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 64, None) == tq.TQ_ERR_WORKSPACE
+    assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2010, 1 << 20, None) == tq.TQ_ERR_WORKSPACE
+    assert A(good.ref, None, 0, 4, 0, None, 100, ctypes.byref(nullbank), 0, None, 0, None) == tq.TQ_OK
+    assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 2, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
     assert L.tq_fp32_logits(None, 1, 10, 128, 0x1000, 4, 0x2000, None) == tq.TQ_ERR_ARG
     assert L.tq_copy(0x1001, 0x2000, 64, None) == tq.TQ_ERR_ARG
     # empty inputs are valid no-ops
