@@ -333,6 +333,47 @@ def append_extra(tq, device):
     return out
 
 
+def variants_extra(tq, device):
+    """One decode8b layer (b=3) encoded and scored with the randomised Walsh-Hadamard rotation
+    and the exact sphere-marginal codebook (same kernels, other parameters)."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    groups = groups_of(cfg, 3)
+    signs = np.where(np.random.default_rng(77).random(cfg.d) < 0.5, -1.0, 1.0).astype(np.float32)
+    prm = tq.make_params(cfg.d, cfg.m, groups, None, workloads.projection(cfg.cfg_id, cfg.m, cfg.d), None, device,
+                         rotations=[tq.tq_make_rotation_hadamard(signs)],
+                         codebooks=[tq.tq_make_codebook_sphere(groups[0][1], cfg.d)[:2]])
+    keys = workloads.keys_device(cfg, 0, device)
+    q = workloads.queries_device(cfg, 0, device)
+    bank = tq.Bank(prm, cfg.banks, cfg.tokens, device)
+    ws = torch.empty(prm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), dtype=torch.uint8, device=device)
+    tq.tq_encode(prm, keys, bank, workspace=ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        tq.tq_encode(prm, keys, bank, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    enc_ms = a.elapsed_time(b) / 3
+    scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+    sws = tq.score_workspace(prm, bank, cfg.G)
+    tq.tq_score(prm, bank, q, scores=scores, workspace=sws)
+    a.record()
+    for _ in range(10):
+        tq.tq_score(prm, bank, q, scores=scores, workspace=sws)
+    b.record()
+    torch.cuda.synchronize()
+    sc_us = a.elapsed_time(b) * 100
+    n = cfg.banks * cfg.tokens
+    return {"workload": "decode8b layer 0, b=3, Walsh-Hadamard rotation + sphere-marginal codebook (d=128)",
+            "encode": encode_rates(n, enc_ms, cfg.d, cfg.m, [cfg.d], True),
+            "score_us_per_launch_same_layer_repeated": sc_us,
+            "codebook_mse_sphere_vs_normal": [tq.tq_make_codebook_sphere(groups[0][1], cfg.d)[2],
+                                              tq.tq_make_codebook(groups[0][1])[2]]}
+
+
 def search_extra(tq, device):
     """Vector search: 2,000,000 x 768 unit vectors, 1024 queries, top-10 per query, at
     b=4 and b=2; encode rate, top-k rate and recall@10 against the exact inner products."""
@@ -515,6 +556,9 @@ def main():
         out["search"] = search_extra(tq, device)
         log("streaming append")
         out["append"] = append_extra(tq, device)
+        torch.cuda.empty_cache()
+        log("rotation / codebook variants")
+        out["variants"] = variants_extra(tq, device)
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

@@ -108,6 +108,20 @@ typedef struct {
  * (host, nullable) receives the fp64 mean squared error. Deterministic. */
 int tq_make_codebook(int bits, float *centroids, float *thresholds, double *mse_out);
 
+/* Lloyd-Max codebook, in the same z units, for the exact distribution of one coordinate
+ * of a uniformly random unit vector in R^d (density proportional to (1 - z^2/d)^((d-3)/2)
+ * on |z| < sqrt(d); the normal distribution is its large-d limit). 1 <= bits <= 4,
+ * 3 <= d <= 2^24, else TQ_ERR_ARG. Host fp64; outputs as tq_make_codebook (symmetric). */
+int tq_make_codebook_sphere(int bits, int d, float *centroids, float *thresholds, double *mse_out);
+
+/* Randomised Walsh-Hadamard rotation (tistory series part 11, on community GPU
+ * implementations: structured Walsh-Hadamard rotations are tried to speed up the rotation):
+ * rot (host) receives d x d floats, entry (j, k) =
+ * (-1)^popcount(j & k) * sign(signs[k]) / sqrt(d). d a power of two, at most 4096; signs
+ * (host) float[d], each nonzero. TQ_ERR_ARG otherwise. The matrix is orthogonal and goes to
+ * tq_params.rot like any other rotation. */
+int tq_make_rotation_hadamard(int d, const float *signs, float *rot);
+
 /* Random orthogonal rotation (same write-up, stage 1): the Q factor of a QR
  * decomposition of the d x d matrix `gauss` (host, row-major, expected i.i.d.
  * N(0,1)), with column signs fixed so that the triangular factor has a positive

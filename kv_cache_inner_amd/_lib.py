@@ -41,7 +41,7 @@ class tq_bank(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("rnorms", ctypes.c_void_p)]
 
 
-EXPORTS = ["tq_make_codebook", "tq_make_rotation", "tq_bank_layout", "tq_workspace_bytes", "tq_encode",
+EXPORTS = ["tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_make_rotation_hadamard", "tq_bank_layout", "tq_workspace_bytes", "tq_encode",
            "tq_encode_append", "tq_prepare_queries", "tq_score_prepared", "tq_score", "tq_topk", "tq_fp32_logits", "tq_copy",
            "tq_status_string"]
 
@@ -56,6 +56,8 @@ def _load():
     sig = {
         "tq_make_codebook": (ctypes.c_int, [ctypes.c_int, vp, vp, vp]),
         "tq_make_rotation": (ctypes.c_int, [ctypes.c_int, vp, vp]),
+        "tq_make_codebook_sphere": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, vp, vp, vp]),
+        "tq_make_rotation_hadamard": (ctypes.c_int, [ctypes.c_int, vp, vp]),
         "tq_bank_layout": (ctypes.c_int, [P, i64, vp, vp, vp]),
         "tq_workspace_bytes": (sz, [ctypes.c_int, P, i64, i64, i32, i32]),
         "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, B, vp, sz, vp]),
@@ -123,6 +125,24 @@ def tq_make_rotation(gauss: np.ndarray) -> np.ndarray:
     return out
 
 
+def tq_make_codebook_sphere(bits: int, d: int) -> Tuple[np.ndarray, np.ndarray, float]:
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(max(L - 1, 1), np.float32)
+    mse = ctypes.c_double()
+    _check("tq_make_codebook_sphere", _lib.tq_make_codebook_sphere(bits, d, c.ctypes.data, t.ctypes.data,
+                                                                   ctypes.addressof(mse)))
+    return c, t[: L - 1], mse.value
+
+
+def tq_make_rotation_hadamard(signs: np.ndarray) -> np.ndarray:
+    s = np.ascontiguousarray(signs, dtype=np.float32)
+    d = s.shape[0]
+    out = np.zeros((d, d), np.float32)
+    _check("tq_make_rotation_hadamard", _lib.tq_make_rotation_hadamard(d, s.ctypes.data, out.ctypes.data))
+    return out
+
+
 class Params:
     """tq_params plus the device tensors it points to (kept alive here)."""
 
@@ -165,16 +185,18 @@ class Params:
 
 
 def make_params(d: int, m: int, groups: Sequence[Tuple[int, int]], gaussians: Sequence[np.ndarray], proj: np.ndarray,
-                chan: Optional[np.ndarray] = None, device="cuda") -> Params:
-    """Host construction of R (tq_make_rotation per group) and the codebooks
-    (tq_make_codebook), uploaded with S and the channel list."""
+                chan: Optional[np.ndarray] = None, device="cuda", rotations: Optional[Sequence[np.ndarray]] = None,
+                codebooks: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None) -> Params:
+    """Host construction of R (tq_make_rotation per group, unless explicit `rotations` are
+    given) and the codebooks (tq_make_codebook unless `codebooks` are given), uploaded with
+    S and the channel list."""
     import torch
 
-    rots = [tq_make_rotation(g) for g in gaussians]
+    rots = list(rotations) if rotations is not None else [tq_make_rotation(g) for g in gaussians]
     rot = torch.from_numpy(np.concatenate([r.ravel() for r in rots])).to(device)
     pj = torch.from_numpy(np.ascontiguousarray(proj, dtype=np.float32)).to(device)
     ch = None if chan is None else torch.from_numpy(np.ascontiguousarray(chan, dtype=np.int32)).to(device)
-    return Params(d, m, groups, rot, pj, ch)
+    return Params(d, m, groups, rot, pj, ch, codebooks=codebooks)
 
 
 class Bank:

@@ -73,6 +73,122 @@ extern "C" int tq_make_codebook(int bits, float *centroids, float *thresholds, d
 }
 
 // ----------------------------------------------------------------------------------------
+// Lloyd-Max codebook for the exact distribution of a rotated coordinate of a unit vector in
+// R^d, in the same units (z = sqrt(d) t). A coordinate t of a uniformly random unit vector
+// has density proportional to (1 - t^2)^((d-3)/2) on [-1, 1]; the normal distribution is
+// its limit for large d (turboquant-pytorch write-up, stage 1: the rotated coordinates
+// follow a bell curve, and the codebook is fitted to that distribution). Same iteration as
+// above on z in [0, sqrt(d)]: the first moment of a cell in closed form, its mass and
+// second moment by composite Gauss-Legendre quadrature (16 panels x 16 points per cell).
+// ----------------------------------------------------------------------------------------
+namespace {
+struct SphereMarginal {
+    double d, e, scale;  // density scale * (1 - z^2/d)^e on |z| < sqrt(d), e = (d - 3)/2
+    explicit SphereMarginal(int dim) : d(dim), e(0.5 * (dim - 3)) {
+        scale = exp(lgamma(0.5 * dim) - lgamma(0.5 * (dim - 1))) / sqrt(M_PI * dim);
+    }
+    double pdf(double z) const {
+        const double x = z * z / d;  // log1p keeps (1 - x)^e accurate for large d
+        return x >= 1.0 ? 0.0 : scale * exp(e * log1p(-x));
+    }
+    // integral over [a, b] of z * pdf(z): scale * d / (d - 1) * [(1 - z^2/d)^(e + 1)] from b to a
+    double first(double a, double b) const {
+        auto g = [&](double z) {
+            const double x = z * z / d;
+            return x >= 1.0 ? 0.0 : exp((e + 1.0) * log1p(-x));
+        };
+        return scale * d / (d - 1.0) * (g(a) - g(b));
+    }
+    // integrals over [a, b] of z^p * pdf(z), p = 0 and 2
+    void masses(double a, double b, double &m0, double &m2) const {
+        static const double x16[8] = {0.0950125098376374, 0.2816035507792589, 0.4580167776572274,
+                                      0.6178762444026438, 0.7554044083550030, 0.8656312023878318,
+                                      0.9445750230732326, 0.9894009349916499};
+        static const double w16[8] = {0.1894506104550685, 0.1826034150449236, 0.1691565193950025,
+                                      0.1495959888165767, 0.1246289712555339, 0.0951585116824928,
+                                      0.0622535239386479, 0.0271524594117541};
+        m0 = m2 = 0.0;
+        const int panels = 16;
+        const double h = (b - a) / panels;
+        for (int pnl = 0; pnl < panels; ++pnl) {
+            const double mid = a + (pnl + 0.5) * h, half = 0.5 * h;
+            for (int k = 0; k < 8; ++k)
+                for (int sgn = -1; sgn <= 1; sgn += 2) {
+                    const double z = mid + sgn * half * x16[k], f = pdf(z) * w16[k] * half;
+                    m0 += f;
+                    m2 += f * z * z;
+                }
+        }
+    }
+};
+}  // namespace
+
+extern "C" int tq_make_codebook_sphere(int bits, int d, float *centroids, float *thresholds, double *mse_out) {
+    if (bits < 1 || bits > 4 || d < 3 || d > (1 << 24) || !centroids || !thresholds) return TQ_ERR_ARG;
+    const SphereMarginal sm(d);
+    const int L = 1 << bits, H = L / 2;
+    // the outer cell ends at sqrt(d), or at 40 when sqrt(d) is larger: the density there is
+    // below exp(-z^2 (d - 3) / (2 d)) <= exp(-200) for d >= 4, so the quadrature panels stay
+    // where the mass is
+    const double top = fmin(sqrt((double)d), 40.0);
+    double c[8], t[9];
+    for (int k = 0; k < H; ++k) c[k] = fmin(3.0, top) * (k + 0.5) / H;  // start: even grid
+    t[0] = 0.0;
+    for (int iter = 0; iter < 200000; ++iter) {
+        for (int k = 1; k < H; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+        t[H] = top;
+        double change = 0.0;
+        for (int k = 0; k < H; ++k) {
+            double m0, m2;
+            sm.masses(t[k], t[k + 1], m0, m2);
+            const double nc = sm.first(t[k], t[k + 1]) / m0;
+            change = fmax(change, fabs(nc - c[k]));
+            c[k] = nc;
+        }
+        if (change < 1e-13) break;  // far below float resolution
+    }
+    for (int k = 1; k < H; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    t[H] = top;
+    double mse = 0.0;
+    for (int k = 0; k < H; ++k) {
+        double m0, m2;
+        sm.masses(t[k], t[k + 1], m0, m2);
+        mse += 2.0 * (m2 - 2.0 * c[k] * sm.first(t[k], t[k + 1]) + c[k] * c[k] * m0);
+    }
+    for (int k = 0; k < H; ++k) {
+        centroids[H + k] = (float)c[k];
+        centroids[H - 1 - k] = -(float)c[k];
+    }
+    for (int k = 0; k < H; ++k) {
+        const float tk = (float)t[k];
+        thresholds[H - 1 + k] = tk;
+        if (k > 0) thresholds[H - 1 - k] = -tk;
+    }
+    if (mse_out) *mse_out = mse;
+    return TQ_OK;
+}
+
+// ----------------------------------------------------------------------------------------
+// Randomised Walsh-Hadamard rotation: R = H_d diag(s) / sqrt(d) with H_d the Sylvester
+// Hadamard matrix (entry (j, k) = (-1)^popcount(j & k)) and s_k = sign(signs[k]); d a power
+// of two. An orthogonal rotation that a fast transform applies in O(d log d) (tistory series
+// part 11, on community GPU implementations: structured Walsh-Hadamard rotations are being
+// tried to speed up the rotation).
+// ----------------------------------------------------------------------------------------
+extern "C" int tq_make_rotation_hadamard(int d, const float *signs, float *rot) {
+    if (d <= 0 || d > 4096 || (d & (d - 1)) || !signs || !rot) return TQ_ERR_ARG;
+    const float inv = (float)(1.0 / sqrt((double)d));
+    for (int k = 0; k < d; ++k)
+        if (!(signs[k] != 0.0f)) return TQ_ERR_ARG;  // zero or NaN: no sign
+    for (int j = 0; j < d; ++j)
+        for (int k = 0; k < d; ++k) {
+            const bool neg = (__builtin_popcount((unsigned)(j & k)) & 1) != (signs[k] < 0.0f);
+            rot[(size_t)j * d + k] = neg ? -inv : inv;
+        }
+    return TQ_OK;
+}
+
+// ----------------------------------------------------------------------------------------
 // Random orthogonal rotation: modified Gram-Schmidt (applied twice per column) on the
 // columns of the Gaussian matrix. The resulting triangular factor has a positive
 // diagonal by construction, which fixes the column signs: this is the unique

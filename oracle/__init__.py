@@ -100,22 +100,89 @@ def rotation(gauss: np.ndarray) -> np.ndarray:
     return out
 
 
-class Params:
-    """The oracle's own parameters: rotations from its own QR, codebooks from its
-    own Lloyd-Max, the projection S as drawn (float32)."""
+def codebook_sphere(bits: int, d: int, tol: float = 1e-14):
+    """Lloyd-Max, in z units (z = sqrt(d) t), for one coordinate t of a uniformly random
+    unit vector in R^d: t^2 ~ Beta(1/2, (d-1)/2), the law of a squared coordinate of a
+    uniform point on the sphere (turboquant-pytorch write-up, stage 1: the codebook is fitted
+    to the distribution of the rotated coordinates; its large-d limit is N(0,1)). Cell
+    masses and moments from the regularised incomplete beta function, the Lloyd fixed
+    point iterated on the positive half (the law is symmetric). Returns
+    (centroids[2^b], thresholds[2^b - 1], mse)."""
+    from scipy.special import betainc, betaln
 
-    def __init__(self, spec: Spec, gaussians: Sequence[np.ndarray], proj: Optional[np.ndarray]):
+    L, H = 1 << bits, 1 << (bits - 1)
+    beta = 0.5 * (d - 1)
+    top = np.sqrt(d)
+
+    def moments(a, b):  # over a <= z <= b, z >= 0: mass, E[z 1], E[z^2 1]
+        ua, ub = min(a * a / d, 1.0), min(b * b / d, 1.0)  # (sqrt(d))^2 / d may round above 1
+        m0 = 0.5 * (betainc(0.5, beta, ub) - betainc(0.5, beta, ua))
+        r1 = np.exp(betaln(1.0, beta) - betaln(0.5, beta))  # E[sqrt(u)] over the whole law
+        m1 = 0.5 * np.sqrt(d) * r1 * (betainc(1.0, beta, ub) - betainc(1.0, beta, ua))
+        m2 = 0.5 * (betainc(1.5, beta, ub) - betainc(1.5, beta, ua))  # E[z^2] = d E[u] = 1 overall
+        return m0, m1, m2
+
+    c = np.array([min(3.0, top) * (k + 0.5) / H for k in range(H)])
+    for _ in range(1_000_000):
+        t = np.concatenate([[0.0], 0.5 * (c[:-1] + c[1:]), [top]])
+        nc = np.array([moments(t[k], t[k + 1])[1] / moments(t[k], t[k + 1])[0] for k in range(H)])
+        done = np.max(np.abs(nc - c)) < tol
+        c = nc
+        if done:
+            break
+    t = np.concatenate([[0.0], 0.5 * (c[:-1] + c[1:]), [top]])
+    mse = 0.0
+    for k in range(H):
+        m0, m1, m2 = moments(t[k], t[k + 1])
+        mse += 2.0 * (m2 - 2.0 * c[k] * m1 + c[k] * c[k] * m0)
+    cent = np.concatenate([-c[::-1], c])
+    thr = np.concatenate([-t[1:H][::-1], [0.0], t[1:H]])
+    return cent, thr, mse
+
+
+def hadamard_rotation(signs: np.ndarray) -> np.ndarray:
+    """Randomised Walsh-Hadamard rotation H_d diag(sign(s)) / sqrt(d), d a power of two,
+    with H_d the Sylvester Hadamard matrix (tistory series part 11, on community GPU
+    implementations: structured Walsh-Hadamard rotations). fp64."""
+    from scipy.linalg import hadamard
+
+    s = np.sign(np.asarray(signs, np.float64))
+    d = s.shape[0]
+    return hadamard(d).astype(np.float64) * s[None, :] / np.sqrt(d)
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform along the last axis (butterflies)."""
+    y = np.array(x, np.float64, copy=True)
+    n, h = y.shape[-1], 1
+    while h < n:
+        y = y.reshape(*y.shape[:-1], n // (2 * h), 2, h)
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, a - b
+        y = y.reshape(*y.shape[:-3], n)
+        h *= 2
+    return y
+
+
+class Params:
+    """The oracle's own parameters: rotations from its own QR (or the given rotation
+    matrices), codebooks from its own Lloyd-Max (or the given (centroids, thresholds) per
+    group), the projection S as drawn (float32)."""
+
+    def __init__(self, spec: Spec, gaussians: Sequence[np.ndarray], proj: Optional[np.ndarray],
+                 rotations: Optional[Sequence[np.ndarray]] = None, codebooks: Optional[Sequence[tuple]] = None):
         self.spec = spec
-        self.rots = [rotation(g) for g in gaussians]
+        self.rots = ([np.asarray(r, np.float64) for r in rotations] if rotations is not None
+                     else [rotation(g) for g in gaussians])
         self.rot = np.ascontiguousarray(np.concatenate([r.ravel() for r in self.rots]))
         m = spec.m
         self.proj = np.ascontiguousarray(proj, dtype=np.float32) if m > 0 else np.zeros((1, spec.d), np.float32)
         self.cent = np.zeros((2, 16), np.float64)
         self.thr = np.zeros((2, 15), np.float32)
         for g, (_, b) in enumerate(spec.groups):
-            c, t, _, _ = codebook(b)
+            c, t = codebooks[g][:2] if codebooks is not None else codebook(b)[:2]
             self.cent[g, : len(c)] = c
-            self.thr[g, : len(t)] = t.astype(np.float32)
+            self.thr[g, : len(t)] = np.asarray(t, np.float64).astype(np.float32)
 
 
 def n_pad(n: int) -> int:

@@ -405,3 +405,46 @@ def test_encode_append_slots(tq, unaligned):
         assert (gn[b][untouched] == -1.0).all() and (gr[b][untouched] == -2.0).all()
     assert len(filled[1]) == 37 + 1 + 7 + (bank.n_pad - n_cap)
     say("report", report)
+
+
+# ------------------------------------------------------------------------------------------
+# variants: randomised Walsh-Hadamard rotation, exact sphere-marginal codebook
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["hadamard", "sphere", "both"])
+def test_variant_encode_and_score(tq, variant):
+    """The kernels take any orthogonal rotation and any symmetric codebook: encoding and
+    scoring with the Walsh-Hadamard rotation and/or the sphere-marginal codebook, each side
+    with its own construction of them."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode3b"]
+    groups = groups_of(cfg, 3)
+    d, m, b = cfg.d, cfg.m, groups[0][1]
+    gauss = workloads.rotation_gaussians(cfg.cfg_id, [d])
+    S = workloads.projection(cfg.cfg_id, m, d)
+    signs = np.where(np.random.default_rng(77).random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+    had, sph = variant in ("hadamard", "both"), variant in ("sphere", "both")
+    gpu = tq.make_params(d, m, groups, gauss, S, None, rotations=[tq.tq_make_rotation_hadamard(signs)] if had else None,
+                         codebooks=[tq.tq_make_codebook_sphere(b, d)[:2]] if sph else None)
+    orc = oracle.Params(oracle.Spec(d, m, groups, None), gauss, S,
+                        rotations=[oracle.hadamard_rotation(signs)] if had else None,
+                        codebooks=[oracle.codebook_sphere(b, d)] if sph else None)
+    keys = workloads.keys(cfg, n=1500, banks=[0, 1])
+    q = workloads.queries(cfg, banks=[0, 1])
+    say(f"variant {variant}: encode")
+    bank = tq.Bank(gpu, 2, 1500)
+    tq.tq_encode(gpu, _dev_keys(cfg, keys), bank)
+    torch.cuda.synchronize()
+    gb = download_bank(bank)
+    rep = {}
+    for bk in range(2):
+        check_encode((gb[0][bk], gb[1][bk], gb[2][bk]), oracle.encode_trace(orc, keys[bk]), orc, 1500, rep)
+    say("report", rep)
+    say(f"variant {variant}: score")
+    refs = [oracle.encode(orc, keys[bk]) for bk in range(2)]
+    ob = upload_bank(tq, gpu, np.stack([r[0] for r in refs]), np.stack([r[1] for r in refs]),
+                     np.stack([r[2] for r in refs]), 1500)
+    got = tq.tq_score(gpu, ob, torch.from_numpy(q).cuda()).cpu().numpy()
+    for bk in range(2):
+        check_scores(got[bk], oracle.score(orc, *refs[bk], 1500, q[bk]), f"bank {bk}")

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol(tq):
     names = _declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     lib = ctypes.CDLL(tq.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -199,3 +199,35 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert L.tq_copy(None, None, 0, None) == tq.TQ_OK
     for code in (0, -1, -2, -3, -4, 9):
         assert isinstance(tq.tq_status_string(code), str)
+
+
+# ------------------------------------------------------------------------------------------
+# host-side variants against the oracle's own constructions
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,d", [(1, 3), (2, 16), (3, 128), (4, 768), (3, 1 << 20)])
+def test_sphere_codebook_matches_the_oracle(tq, bits, d):
+    import oracle
+
+    c, t, mse = tq.tq_make_codebook_sphere(bits, d)
+    co, to, mo = oracle.codebook_sphere(bits, d)
+    assert np.abs(c - co).max() < 1e-6 and np.abs(t - to).max() < 1e-6 and abs(mse - mo) < 1e-8
+    assert (c[::-1] == -c).all()
+
+
+def test_hadamard_rotation_matches_the_oracle(tq):
+    import oracle
+
+    g = np.random.default_rng(3)
+    for d in (1, 4, 128, 1024):
+        s = np.where(g.standard_normal(d) > 0, 1.0, -0.5).astype(np.float32)  # only the signs count
+        np.testing.assert_allclose(tq.tq_make_rotation_hadamard(s), oracle.hadamard_rotation(s), atol=1e-7)
+    L = tq._lib.lib()
+    ones = np.ones(8, np.float32)
+    out = np.zeros(64, np.float32)
+    assert L.tq_make_rotation_hadamard(6, ones.ctypes.data, out.ctypes.data) == tq.TQ_ERR_ARG  # not a power of 2
+    ones[3] = 0.0
+    assert L.tq_make_rotation_hadamard(8, ones.ctypes.data, out.ctypes.data) == tq.TQ_ERR_ARG  # a zero sign
+    c = np.zeros(16, np.float32)
+    assert L.tq_make_codebook_sphere(2, 2, c.ctypes.data, c.ctypes.data, None) == tq.TQ_ERR_ARG
+    assert L.tq_make_codebook_sphere(5, 128, c.ctypes.data, c.ctypes.data, None) == tq.TQ_ERR_ARG

@@ -368,6 +368,100 @@ def test_distortion_equals_sphere_marginal_expectation(bits):
 
 
 # ------------------------------------------------------------------------------------
+# variants: the exact sphere-marginal codebook, the randomised Walsh-Hadamard rotation
+# ------------------------------------------------------------------------------------
+
+def _sphere_law_mse(c, t, d):
+    """E[(z - Q(z))^2] under the sphere marginal of z = sqrt(d) u_1 for the codebook (c, t),
+    by adaptive quadrature of the density."""
+    logB = math.lgamma(0.5) + math.lgamma((d - 1) / 2) - math.lgamma(d / 2)
+    f = lambda s: math.exp(((d - 3) / 2) * math.log1p(-min(s * s / d, 1.0)) - logB) / math.sqrt(d)
+    edges = np.concatenate([[-math.sqrt(d)], t, [math.sqrt(d)]])
+    return sum(integrate.quad(lambda s: (s - c[k]) ** 2 * f(s), edges[k], edges[k + 1], epsabs=1e-13,
+                              epsrel=1e-11)[0] for k in range(len(c)))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_sphere_codebook_in_three_dimensions_is_the_uniform_quantiser(bits):
+    # d = 3: a coordinate of a uniform point on the 2-sphere is uniform on [-1, 1]
+    # (Archimedes), so z is uniform on [-sqrt 3, sqrt 3], whose optimal quantiser is uniform
+    L = 1 << bits
+    c, t, mse = oracle.codebook_sphere(bits, 3)
+    r3 = math.sqrt(3.0)
+    np.testing.assert_allclose(c, r3 * (2 * np.arange(L) + 1 - L) / L, atol=1e-12)
+    np.testing.assert_allclose(t, r3 * (2 * np.arange(1, L) - L) / L, atol=1e-12)
+    assert abs(mse - 1.0 / L ** 2) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_sphere_codebook_tends_to_the_normal_one(bits):
+    c, t, mse = oracle.codebook_sphere(bits, 10 ** 8)
+    cg, tg, mg, _ = oracle.codebook(bits)
+    assert np.abs(c - cg).max() < 1e-5 and np.abs(t - tg).max() < 1e-5 and abs(mse - mg) < 1e-6
+
+
+@pytest.mark.parametrize("bits,d", [(2, 8), (3, 16), (3, 128), (4, 32)])
+def test_sphere_codebook_by_quadrature(bits, d):
+    c, t, mse = oracle.codebook_sphere(bits, d)
+    # the distortion by adaptive quadrature of the density (not the beta moments)
+    assert abs(_sphere_law_mse(c, t, d) - mse) < 1e-9
+    # centroid conditions by quadrature: c_k = E[z | cell k]
+    logB = math.lgamma(0.5) + math.lgamma((d - 1) / 2) - math.lgamma(d / 2)
+    f = lambda s: math.exp(((d - 3) / 2) * math.log1p(-min(s * s / d, 1.0)) - logB) / math.sqrt(d)
+    edges = np.concatenate([[-math.sqrt(d)], t, [math.sqrt(d)]])
+    for k in range(len(c)):
+        m0 = integrate.quad(f, edges[k], edges[k + 1], epsabs=1e-14)[0]
+        m1 = integrate.quad(lambda s: s * f(s), edges[k], edges[k + 1], epsabs=1e-14)[0]
+        assert abs(m1 / m0 - c[k]) < 1e-9
+    # and it beats the normal codebook on this law
+    cg, tg, _, _ = oracle.codebook(bits)
+    assert mse < _sphere_law_mse(cg, tg, d)
+
+
+def test_sphere_codebook_is_the_monte_carlo_optimum():
+    """Lloyd on coordinates of sampled uniform unit vectors (d = 12) reaches the same codebook."""
+    d, bits = 12, 2
+    g = np.random.default_rng(5)
+    x = g.standard_normal((100000, d))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    z = (math.sqrt(d) * x).ravel()
+    z = np.concatenate([z, -z])  # the law is symmetric; so is its sample, then
+    c, t, mse = oracle.codebook_sphere(bits, d)
+    ce, te, msee, _ = oracle.lloyd_empirical(z, 1 << bits, oracle.codebook(bits)[0])
+    assert np.abs(ce - c).max() < 3e-3 and abs(msee / len(z) - mse) < 1e-3
+
+
+@pytest.mark.parametrize("d", [1, 2, 8, 128])
+def test_hadamard_rotation_is_orthogonal_and_the_fast_transform(d):
+    g = np.random.default_rng(d)
+    s = np.where(g.standard_normal(d) > 0, 1.0, -1.0)
+    R = oracle.hadamard_rotation(s)
+    np.testing.assert_allclose(R @ R.T, np.eye(d), atol=1e-13)
+    assert np.allclose(np.abs(R), 1 / math.sqrt(d))
+    x = g.standard_normal((5, d))
+    np.testing.assert_allclose(x @ R.T, oracle.fwht(x * s) / math.sqrt(d), atol=1e-12)
+    # entry (j, k) = (-1)^popcount(j & k) s_k / sqrt(d)
+    j, k = g.integers(0, d, 2)
+    assert R[j, k] * math.sqrt(d) == (-1) ** bin(int(j) & int(k)).count("1") * s[k]
+
+
+def test_hadamard_rotation_three_bit_distortion():
+    """The rotated coordinates of Gaussian keys are Gaussian for any fixed rotation, so the
+    3-bit distortion with a Walsh-Hadamard rotation is the reported value too."""
+    d, b, n = 128, 3, 6000
+    g = np.random.default_rng(12)
+    spec = oracle.Spec(d, 0, [(d, b)])
+    prm = oracle.Params(spec, [], None, rotations=[oracle.hadamard_rotation(np.where(g.random(d) > 0.5, 1, -1))])
+    x = g.standard_normal((n, d))
+    x = (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+    bits_, norms, _ = oracle.encode(prm, x)
+    err = ((x.astype(np.float64) - oracle.decode(prm, bits_, norms, n)) ** 2).sum(axis=1)
+    se = err.std() / math.sqrt(n)
+    assert abs(err.mean() - _sphere_marginal_mse(b, d)) < 4 * se + 1e-5
+    assert round(err.mean(), 3) == 0.034
+
+
+# ------------------------------------------------------------------------------------
 # the estimator: unbiased, with the sign sketch's closed-form variance; MSE-only is biased
 # ------------------------------------------------------------------------------------
 
