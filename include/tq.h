@@ -58,7 +58,7 @@ typedef enum {
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
-typedef enum { TQ_OP_ENCODE = 0, TQ_OP_SCORE = 1, TQ_OP_TOPK = 2 } tq_op;
+typedef enum { TQ_OP_ENCODE = 0, TQ_OP_SCORE = 1, TQ_OP_TOPK = 2, TQ_OP_ATTEND = 3 } tq_op;
 
 /* tq_encode_append flags. TQ_APPEND_PREPARED: the workspace already holds this call's
  * folded projection S' = S P_chan blockdiag(R_g)^T, written by an earlier tq_encode or
@@ -68,7 +68,9 @@ enum { TQ_APPEND_PREPARED = 1 };
 /* Parameters of one encoding. Dimensions and the codebooks are host values;
  * the matrices are (device) pointers read by the kernels.
  *   d            key dimension; d = group_dim[0] (+ group_dim[1])
- *   m            sign-sketch rows (QJL); a multiple of 32, >= 32
+ *   m            sign-sketch rows (QJL): a multiple of 32 in [32, 1024], or 0 for the
+ *                MSE-only quantiser (codes and norms only; such banks can be decoded and
+ *                attended over as values, not scored: TQ_ERR_UNSUPPORTED)
  *   n_groups     1, or 2 for a split of the channels into two groups that are
  *                rotated and quantised separately (mixed bit widths)
  *   group_dim    channels per group, multiples of 32
@@ -82,7 +84,8 @@ enum { TQ_APPEND_PREPARED = 1 };
  *                NULL = identity (required NULL when n_groups == 1)
  *   rot          (device) float32: group 0's d_0 x d_0 rotation row-major, then
  *                group 1's; rotated coordinate j of group g = row j . x_g
- *   proj         (device) float32 [m][d] row-major: S, columns in channel order */
+ *   proj         (device) float32 [m][d] row-major: S, columns in channel order (NULL
+ *                when m == 0) */
 typedef struct {
     int32_t d, m, n_groups;
     int32_t group_dim[2];
@@ -197,6 +200,27 @@ int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, co
  * per row of four queries. */
 int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, const float *q, int32_t G, int32_t k,
             float *vals, int32_t *idx, void *workspace, size_t ws_bytes, void *stream);
+
+/* Decompression of the stage-1 part (turboquant-pytorch write-up, usage example: decompress;
+ * the MSE quantiser's reconstruction): out (device) float32 [banks][n][d], per stored vector
+ * and channel group x_hat_g = (nu_g / sqrt(d_g)) R_g^T c_g[idx_g], in channel order. The sign
+ * sketch, if any, is not used. fp32 arithmetic (relative error about d_g * 2^-24). */
+int tq_decode(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, float *out, void *stream);
+
+/* Decode attention over a packed KV cache (same write-up, usage example: keys held by the
+ * inner-product quantiser, values by the MSE quantiser): for bank b and query row g,
+ *   out[b][g] = sum_i softmax_i(scale * est(q[b][g], key_i)) * x_hat(value_i),
+ * est as tq_score returns it (fp32) and x_hat as tq_decode forms it. keys: a bank of n
+ * tokens under kp (m > 0); values: a bank of the same n tokens under vp (any m; the sketch
+ * is ignored), d_v = vp->d <= 128 (else TQ_ERR_UNSUPPORTED). q (device) float32
+ * [banks][G][kp->d], out (device) float32 [banks][G][d_v]. n >= 1, finite scale, else
+ * TQ_ERR_ARG. The logits are formed into `workspace` (device) of
+ * tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0) bytes, 256-byte aligned
+ * (TQ_ERR_WORKSPACE otherwise), then reduced per chunk of 1024 tokens (softmax weights in
+ * 30-bit fixed point, exact integer products) and merged in fp64. */
+int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_params *vp, const tq_bank *values, int64_t banks,
+              int64_t n, const float *q, int32_t G, float scale, float *out, void *workspace, size_t ws_bytes,
+              void *stream);
 
 /* Measurement kernels (not part of the method):
  * fp32 logits against unquantized keys, scores[b][g][i] = q[b][g] . keys[b][i]

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtq.so")
 
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_DEVICE, TQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
 TQ_F32, TQ_BF16 = 0, 1
-TQ_OP_ENCODE, TQ_OP_SCORE, TQ_OP_TOPK = 0, 1, 2
+TQ_OP_ENCODE, TQ_OP_SCORE, TQ_OP_TOPK, TQ_OP_ATTEND = 0, 1, 2, 3
 TQ_APPEND_PREPARED = 1
 
 
@@ -41,8 +41,9 @@ class tq_bank(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("rnorms", ctypes.c_void_p)]
 
 
-EXPORTS = ["tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_make_rotation_hadamard", "tq_bank_layout", "tq_workspace_bytes", "tq_encode",
-           "tq_encode_append", "tq_prepare_queries", "tq_score_prepared", "tq_score", "tq_topk", "tq_fp32_logits", "tq_copy",
+EXPORTS = ["tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_make_rotation_hadamard",
+           "tq_bank_layout", "tq_workspace_bytes", "tq_encode", "tq_encode_append", "tq_prepare_queries",
+           "tq_score_prepared", "tq_score", "tq_topk", "tq_decode", "tq_attend", "tq_fp32_logits", "tq_copy",
            "tq_status_string"]
 
 
@@ -66,6 +67,8 @@ def _load():
         "tq_score_prepared": (ctypes.c_int, [P, B, i64, i64, i32, vp, vp, vp]),
         "tq_score": (ctypes.c_int, [P, B, i64, i64, vp, i32, vp, vp, sz, vp]),
         "tq_topk": (ctypes.c_int, [P, B, i64, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
+        "tq_decode": (ctypes.c_int, [P, B, i64, i64, vp, vp]),
+        "tq_attend": (ctypes.c_int, [P, B, P, B, i64, i64, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
         "tq_fp32_logits": (ctypes.c_int, [vp, i64, i64, i32, vp, i32, vp, vp]),
         "tq_copy": (ctypes.c_int, [vp, vp, sz, vp]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -194,7 +197,7 @@ def make_params(d: int, m: int, groups: Sequence[Tuple[int, int]], gaussians: Se
 
     rots = list(rotations) if rotations is not None else [tq_make_rotation(g) for g in gaussians]
     rot = torch.from_numpy(np.concatenate([r.ravel() for r in rots])).to(device)
-    pj = torch.from_numpy(np.ascontiguousarray(proj, dtype=np.float32)).to(device)
+    pj = None if proj is None else torch.from_numpy(np.ascontiguousarray(proj, dtype=np.float32)).to(device)
     ch = None if chan is None else torch.from_numpy(np.ascontiguousarray(chan, dtype=np.int32)).to(device)
     return Params(d, m, groups, rot, pj, ch, codebooks=codebooks)
 
@@ -301,6 +304,38 @@ def tq_topk(params: Params, bank: Bank, q, k: int, workspace=None, stream=None):
     _check("tq_topk", _lib.tq_topk(params.ref, bank.ref, bank.banks, bank.n, q.data_ptr(), G, k, vals.data_ptr(),
                                    idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
     return vals, idx
+
+
+def tq_decode(params: Params, bank: Bank, out=None, stream=None):
+    """Stage-1 reconstruction x_hat [banks, n, d] (float32, channel order) of a packed bank."""
+    import torch
+
+    if out is None:
+        out = torch.empty((bank.banks, bank.n, params.d), dtype=torch.float32, device=bank.bits.device)
+    _check("tq_decode", _lib.tq_decode(params.ref, bank.ref, bank.banks, bank.n, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def attend_workspace(kparams: Params, bank: Bank, G: int):
+    return _workspace(kparams.workspace_bytes(TQ_OP_ATTEND, bank.banks, bank.n, G), bank.bits.device)
+
+
+def tq_attend(kparams: Params, kbank: Bank, vparams: Params, vbank: Bank, q, scale: float, out=None, workspace=None,
+              stream=None):
+    """Decode attention: softmax(scale * estimated logits) over the tokens of each bank,
+    applied to the decompressed values. q [banks, G, d_k] -> out [banks, G, d_v]."""
+    import torch
+
+    assert q.is_contiguous() and q.dim() == 3 and q.shape[0] == kbank.banks and q.shape[2] == kparams.d
+    assert vbank.banks == kbank.banks and vbank.n == kbank.n
+    G = q.shape[1]
+    if out is None:
+        out = torch.empty((kbank.banks, G, vparams.d), dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else attend_workspace(kparams, kbank, G)
+    _check("tq_attend", _lib.tq_attend(kparams.ref, kbank.ref, vparams.ref, vbank.ref, kbank.banks, kbank.n,
+                                       q.data_ptr(), G, float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       _stream(stream)))
+    return out
 
 
 def tq_fp32_logits(keys, q, scores=None, stream=None):

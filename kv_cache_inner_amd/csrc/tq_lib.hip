@@ -13,6 +13,7 @@
 #include "tq_encode_gemm.h"
 #include "tq_score.h"
 #include "tq_topk.h"
+#include "tq_attend.h"
 #include "tq_measure.h"
 
 using namespace tq;
@@ -241,8 +242,9 @@ static int check_params(const tq_params *p) {
                 return TQ_ERR_ARG;
     }
     if (sum != p->d || p->d > 1024) return TQ_ERR_ARG;
-    if (p->m < 32 || p->m > 1024 || p->m % 32) return TQ_ERR_ARG;
-    if (!p->rot || !p->proj) return TQ_ERR_ARG;
+    // m = 0: codes and norms only (the MSE-only quantiser, e.g. for stored values)
+    if (p->m != 0 && (p->m < 32 || p->m > 1024 || p->m % 32)) return TQ_ERR_ARG;
+    if (!p->rot || (p->m > 0 && !p->proj)) return TQ_ERR_ARG;
     return TQ_OK;
 }
 
@@ -373,10 +375,30 @@ static size_t topk_part_bytes(int64_t banks, int32_t G, int kchunks, int32_t k) 
     return align256((size_t)banks * G * kchunks * LDS_WAVES * k * 4);
 }
 
+// attention workspace: logits [banks][G][n] | scorer workspace | chunk partials
+// [banks][G][chunks][2 + AT_DMAX]
+struct AttnWs {
+    size_t score_off, score_bytes, part_off, total;
+};
+static AttnWs attn_ws_layout(size_t score_bytes, int64_t banks, int64_t n, int32_t G) {
+    AttnWs w;
+    w.score_off = align256((size_t)banks * G * n * 4);
+    w.score_bytes = score_bytes;
+    w.part_off = w.score_off + align256(score_bytes);
+    const int64_t chunks = (n + AT_CHUNK - 1) / AT_CHUNK;
+    w.total = w.part_off + align256((size_t)banks * G * chunks * (2 + AT_DMAX) * 4);
+    return w;
+}
+
 extern "C" size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k) {
     if (check_params(p) || banks < 0 || n < 0) return 0;
     if (op == TQ_OP_ENCODE) return enc_ws_layout(p, banks, n).total;
     if (G < 1) return 0;
+    if (op == TQ_OP_ATTEND) {
+        if (p->m == 0 || n < 1) return 0;
+        const size_t sb = tq_workspace_bytes(TQ_OP_SCORE, p, banks, n, G, 0);
+        return sb ? attn_ws_layout(sb, banks, n, G).total : 0;
+    }
     size_t out = 0;
     const int rc = with_layout(p, [&](auto l) {
         using L = decltype(l);
@@ -425,6 +447,7 @@ static EncArgs enc_args(const tq_params *p) {
 }
 
 static void launch_prep_proj(const tq_params *p, const EncArgs &a, float *sp, hipStream_t st) {
+    if (p->m == 0) return;  // no sketch, no S'
     const int bx = p->d <= 64 ? 64 : (p->d <= 128 ? 128 : 256);
     hipLaunchKernelGGL(enc_prep_proj_kernel, dim3((unsigned)((p->d + bx - 1) / bx), (unsigned)p->m), dim3(bx), 0, st,
                        p->proj, p->rot, p->group_chan, a, sp);
@@ -439,6 +462,7 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (!keys || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
     const EncWs ew = enc_ws_layout(p, banks, n);
     if (!workspace || ws_bytes < ew.total || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    if (p->m == 0 && enc_large(p)) return TQ_ERR_UNSUPPORTED;  // MSE-only keys up to 128 dimensions
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
@@ -598,6 +622,7 @@ extern "C" int tq_prepare_queries(const tq_params *p, const float *q, int64_t ba
                                   size_t ws_bytes, void *stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0) return TQ_OK;
     if (!q) return TQ_ERR_ARG;
@@ -740,6 +765,7 @@ extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t 
                                  const void *workspace, float *scores, void *stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores) return TQ_ERR_ARG;
@@ -767,6 +793,7 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
                         float *scores, void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q) return TQ_ERR_ARG;
@@ -795,6 +822,7 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
                        int32_t k, float *vals, int32_t *idx, void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1 || k < 1 || k > 64 || k > n) return TQ_ERR_ARG;
     if (banks == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx) return TQ_ERR_ARG;
@@ -822,6 +850,120 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
             return launch_status();
         }
     });
+}
+
+// ----------------------------------------------------------------------------------------
+// decompression and decode attention
+// ----------------------------------------------------------------------------------------
+static DecArgs dec_args(const tq_params *p) {
+    DecArgs a;
+    memset(&a, 0, sizeof(a));
+    a.d = p->d;
+    a.ng = p->n_groups;
+    a.W = words_per_key(p);
+    int off = 0, word = 0;
+    for (int g = 0; g < p->n_groups; ++g) {
+        a.gdim[g] = p->group_dim[g];
+        a.gbits[g] = p->group_bits[g];
+        a.goff[g] = off;
+        a.gword[g] = word;
+        off += p->group_dim[g];
+        word += p->group_bits[g] * p->group_dim[g] / 32;
+        for (int i = 0; i < (1 << p->group_bits[g]); ++i) a.cent[g][i] = p->centroids[g][i];
+        a.inv_sqrt_d[g] = (float)(1.0 / sqrt((double)p->group_dim[g]));
+    }
+    return a;
+}
+
+extern "C" int tq_decode(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, float *out, void *stream) {
+    const int rc = check_params(p);
+    if (rc) return rc;
+    if (banks < 0 || n < 0) return TQ_ERR_ARG;
+    if (banks == 0 || n == 0) return TQ_OK;
+    if (!in || !in->bits || !in->norms || !out) return TQ_ERR_ARG;
+    const int64_t n_tiles = (n + 15) / 16;
+    if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+    const DecArgs a = dec_args(p);
+    hipLaunchKernelGGL(decode_kernel, dim3((unsigned)(banks * n_tiles)), dim3(256), (size_t)16 * p->d * 4,
+                       (hipStream_t)stream, in->bits, in->norms, (long)n, (int)n_tiles, p->rot, p->group_chan, a, out);
+    return launch_status();
+}
+
+// Walsh coefficients a_P of a symmetric codebook in the bit-plane basis the attention kernel
+// uses (planes: bit 0, bit 1, bit 2, and the xor of the three for 3 bits):
+// c[idx] = sum_P a_P s_P(idx), s_P = +-1. False if the codebook is not reproduced.
+static bool attn_args(const tq_params *p, AttnArgs *a) {
+    memset(a, 0, sizeof(*a));
+    a->d = p->d;
+    a->ng = p->n_groups;
+    a->W = words_per_key(p);
+    int off = 0, word = 0;
+    for (int g = 0; g < p->n_groups; ++g) {
+        const int b = p->group_bits[g], L = 1 << b;
+        a->gdim[g] = p->group_dim[g];
+        a->gbits[g] = b;
+        a->goff[g] = off;
+        a->gword[g] = word;
+        off += p->group_dim[g];
+        word += b * p->group_dim[g] / 32;
+        a->inv_sqrt_d[g] = 1.0 / sqrt((double)p->group_dim[g]);
+        auto sgn = [&](int P, int idx) -> double {
+            if (P < 3) return ((idx >> P) & 1) ? 1.0 : -1.0;
+            return (((idx ^ (idx >> 1) ^ (idx >> 2)) & 1) ? 1.0 : -1.0);  // s0 s1 s2 = 2 (b0^b1^b2) - 1
+        };
+        const int planes = b == 3 ? 4 : b;
+        double al[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int P = 0; P < planes; ++P)
+            for (int idx = 0; idx < L; ++idx) al[P] += (double)p->centroids[g][idx] * sgn(P, idx) / L;
+        for (int idx = 0; idx < L; ++idx) {
+            double r = 0.0;
+            for (int P = 0; P < planes; ++P) r += al[P] * sgn(P, idx);
+            const double c = p->centroids[g][idx];
+            if (fabs(r - c) > 1e-6 * (1.0 + fabs(c))) return false;
+        }
+        for (int P = 0; P < planes; ++P) {
+            a->coef[g][P] = 2.0 * al[P];
+            a->bias[g] += al[P];
+        }
+    }
+    return true;
+}
+
+extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_params *vp, const tq_bank *values,
+                         int64_t banks, int64_t n, const float *q, int32_t G, float scale, float *out, void *workspace,
+                         size_t ws_bytes, void *stream) {
+    int rc = check_params(kp);
+    if (rc) return rc;
+    if ((rc = check_params(vp))) return rc;
+    if (kp->m == 0) return TQ_ERR_UNSUPPORTED;  // the logits come from the estimator
+    if (banks < 0 || n < 1 || G < 1 || !isfinite(scale)) return TQ_ERR_ARG;
+    if (vp->d > AT_DMAX) return TQ_ERR_UNSUPPORTED;
+    if (banks == 0) return TQ_OK;
+    if (!keys || !keys->bits || !keys->norms || !keys->rnorms || !values || !values->bits || !values->norms || !q ||
+        !out)
+        return TQ_ERR_ARG;
+    if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    const size_t need = tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0);
+    if (!need) return TQ_ERR_UNSUPPORTED;
+    if (ws_bytes < need) return TQ_ERR_WORKSPACE;
+    const int64_t chunks = (n + AT_CHUNK - 1) / AT_CHUNK;
+    if (banks * chunks > INT32_MAX || banks * G > INT32_MAX || (G + 3) / 4 > 65535) return TQ_ERR_UNSUPPORTED;
+    AttnArgs a;
+    if (!attn_args(vp, &a)) return TQ_ERR_UNSUPPORTED;
+    const AttnWs w = attn_ws_layout(tq_workspace_bytes(TQ_OP_SCORE, kp, banks, n, G, 0), banks, n, G);
+    float *logits = (float *)workspace;
+    float *part = (float *)((char *)workspace + w.part_off);
+    if ((rc = tq_score(kp, keys, banks, n, q, G, logits, (char *)workspace + w.score_off, w.score_bytes, stream)))
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t n_tiles = (n + 15) / 16;
+    hipLaunchKernelGGL(attn_chunk_kernel, dim3((unsigned)(banks * chunks), (unsigned)((G + 3) / 4)), dim3(AT_THREADS),
+                       0, st, logits, values->bits, values->norms, (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a,
+                       part);
+    if ((rc = launch_status())) return rc;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(AT_DMAX), 0, st, part, (int)chunks,
+                       vp->rot, vp->group_chan, a, out);
+    return launch_status();
 }
 
 extern "C" int tq_fp32_logits(const float *keys, int64_t banks, int64_t n, int32_t d, const float *q, int32_t G,

@@ -234,6 +234,24 @@ def decode(prm: Params, bits: np.ndarray, norms: np.ndarray, n: int) -> np.ndarr
     return out
 
 
+def attend(kprm: Params, kbank, vprm: Params, vbank, n: int, q: np.ndarray, scale: float) -> np.ndarray:
+    """Decode attention of queries q [G, d_k] over one bank of n stored tokens (fp64):
+    out [G, d_v] = softmax(scale * est) @ xhat_v.
+
+    turboquant-pytorch write-up (discuss.pytorch.kr), usage example and the two-stage
+    section: the keys are held by the inner-product quantiser, whose estimates est =
+    score(...) stand in for the logits q . k; the values are held by the MSE quantiser and
+    enter through its decompression xhat_v = decode(...). The softmax and the weighted sum
+    are the ordinary attention definition. kbank / vbank: (bits, norms, rnorms) of one bank."""
+    s = score(kprm, kbank[0], kbank[1], kbank[2], n, q)
+    v = decode(vprm, vbank[0], vbank[1], n)
+    z = scale * s
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
 def unpack(spec: Spec, bits: np.ndarray, n: int):
     codes = np.zeros((n, spec.d), np.int32)
     signs = np.zeros((n, max(spec.m, 1)), np.uint8)

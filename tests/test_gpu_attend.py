@@ -1,0 +1,231 @@
+"""Decompression (tq_decode) and decode attention (tq_attend) on the GPU against the oracle.
+
+Both sides read identical bank bytes: the oracle encodes keys (inner-product quantiser)
+and values (MSE-only quantiser, m = 0), the bytes are uploaded, and the GPU output is
+compared with oracle.decode / oracle.attend on the same bytes.
+
+Tolerances, derived from the arithmetic:
+  - decode: fp32 accumulation of d_g products per channel,
+    |x_gpu - x| <= 4 d_g 2^-24 (nu_g / sqrt(d_g)) sum_j |R_g[j][k]| max|c_g|;
+  - attend: the logits the GPU uses differ from the oracle's by at most e (measured here
+    with tq_score on the same bytes, and itself checked against the score tolerance).
+    Perturbing every logit by at most e moves each softmax weight by a factor within
+    e^(+-2 scale e), so |o_gpu - o| <= (e^(2 scale e) - 1) A + 1e-6 (A + s) with
+    A_j = sum_i p_i |x_hat_ij| and s the rms decoded value coordinate: the second term
+    covers the kernel's own rounding (30-bit fixed-point weights, fp32 partials).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import both_params, check_scores, upload_bank
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import kv_cache_inner_amd as tq
+
+    return tq
+
+
+def value_params(tq, cfg, groups, chan=None, layer=0, d=None):
+    """MSE-only (m = 0) parameters for the values, both sides, from the value rotation draws."""
+    d = cfg.d if d is None else d
+    gauss = workloads.value_rotation_gaussians(cfg.cfg_id, [g[0] for g in groups], layer)
+    gpu = tq.make_params(d, 0, groups, gauss, None, chan)
+    orc = oracle.Params(oracle.Spec(d, 0, groups, chan), gauss, None)
+    return gpu, orc
+
+
+def _encode_banks(orc, x):
+    refs = [oracle.encode(orc, x[b]) for b in range(x.shape[0])]
+    return [np.stack([r[i] for r in refs]) for i in range(3)]
+
+
+def _decode_tol(orc, norms_b, n):
+    """Per (vector, channel) bound of the fp32 decoder's rounding (channel order)."""
+    sp = orc.spec
+    tol = np.zeros((n, sp.d))
+    off = 0
+    for g, (dg, b) in enumerate(sp.groups):
+        colsum = np.abs(orc.rots[g]).sum(axis=0)  # sum_j |R[j][k]|
+        cmax = np.abs(orc.cent[g, : 1 << b]).max()
+        t = 4 * dg * 2.0 ** -24 * (norms_b[:n, g:g + 1].astype(np.float64) / np.sqrt(dg)) * colsum[None] * cmax
+        chans = sp.chan[off:off + dg] if sp.chan is not None else np.arange(off, off + dg)
+        tol[:, chans] = t
+        off += dg
+    return tol
+
+
+def _check_attend(got, ref, v, p, e, scale, what):
+    A = p @ np.abs(v)                           # [G, d]
+    s = np.sqrt((v ** 2).mean())
+    tol = (np.expm1(2 * scale * e)) * A + 1e-6 * (A + s)
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} beyond tolerance; worst excess "
+                           f"{np.max(err - tol):.3e}, max err {err.max():.3e}, logit err {e:.3e}")
+    return float(err.max())
+
+
+def _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, scale, n, banks_to_check=None):
+    """Runs tq_attend and tq_score on uploaded banks; compares every (checked) bank with the oracle."""
+    import torch
+
+    banks = kb[0].shape[0]
+    kbank = upload_bank(tq, kgpu, kb[0], kb[1], kb[2], n)
+    vbank = upload_bank(tq, vgpu, vb[0], vb[1], vb[2], n)
+    qd = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+    out = tq.tq_attend(kgpu, kbank, vgpu, vbank, qd, scale).cpu().numpy()
+    logits = tq.tq_score(kgpu, kbank, qd).cpu().numpy()
+    worst = 0.0
+    for b in (range(banks) if banks_to_check is None else banks_to_check):
+        s_ref = oracle.score(korc, kb[0][b], kb[1][b], kb[2][b], n, q[b])
+        e = check_scores(logits[b], s_ref, f"logits bank {b}")
+        v = oracle.decode(vorc, vb[0][b], vb[1][b], n)
+        z = scale * s_ref
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ref = oracle.attend(korc, (kb[0][b], kb[1][b], kb[2][b]), vorc, (vb[0][b], vb[1][b], vb[2][b]), n, q[b], scale)
+        worst = max(worst, _check_attend(out[b], ref, v, p, e, scale, f"bank {b}"))
+    return worst
+
+
+# ------------------------------------------------------------------------------------------
+# decompression
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["keys_b4", "values_b3", "values_b1", "two_groups", "d768"])
+def test_decode_matches_oracle(tq, case):
+    import dataclasses
+
+    cfg = workloads.CONFIGS["decode8b"]
+    n = 1000
+    if case == "keys_b4":
+        gpu, orc = both_params(cfg, 4)
+        x = workloads.keys(cfg, n=n, banks=[0, 5])
+    elif case == "d768":
+        scfg = workloads.CONFIGS["search"]
+        gpu, orc = both_params(scfg, 2)
+        x = workloads.keys(scfg, n=100, banks=[0])
+        n = 100
+    elif case == "two_groups":
+        lcfg = workloads.CONFIGS["longctx"]
+        chan = workloads.group_channels(lcfg)
+        gpu, orc = value_params(tq, lcfg, [(32, 3), (96, 2)], chan)
+        x = workloads.values(lcfg, n=n, banks=[3])
+    else:
+        bits = 3 if case == "values_b3" else 1
+        gpu, orc = value_params(tq, cfg, [(cfg.d, bits)])
+        x = workloads.values(cfg, n=n, banks=[1, 2])
+    say(f"decode {case}: {x.shape}")
+    bits_, norms, rnorms = _encode_banks(orc, x)
+    bank = upload_bank(tq, gpu, bits_, norms, rnorms, n)
+    got = tq.tq_decode(gpu, bank).cpu().numpy()
+    for b in range(x.shape[0]):
+        ref = oracle.decode(orc, bits_[b], norms[b], n)
+        tol = _decode_tol(orc, norms[b], n)
+        err = np.abs(got[b].astype(np.float64) - ref)
+        assert (err <= tol).all(), f"bank {b}: worst excess {np.max(err - tol):.3e}, max err {err.max():.3e}"
+
+
+# ------------------------------------------------------------------------------------------
+# decode attention
+# ------------------------------------------------------------------------------------------
+
+def test_attend_several_chunks_ragged(tq):
+    """3 banks x 2500 tokens (two full 1024-token chunks and a ragged one, a ragged last
+    tile), G = 6 (a full and a partial group of four queries), 3-bit keys + sketch, 3-bit
+    values."""
+    cfg = workloads.CONFIGS["decode8b"]
+    n, G = 2500, 6
+    say(f"attend 3 banks x {n}, G={G}")
+    kgpu, korc = both_params(cfg, 4)
+    vgpu, vorc = value_params(tq, cfg, [(cfg.d, 3)])
+    kb = _encode_banks(korc, workloads.keys(cfg, n=n, banks=[0, 9, 63]))
+    vb = _encode_banks(vorc, workloads.values(cfg, n=n, banks=[0, 9, 63]))
+    q = workloads.queries(cfg, banks=[0, 9, 63], G=G)
+    say("max err", _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, 1.0 / np.sqrt(cfg.d), n))
+
+
+@pytest.mark.parametrize("case", ["v1", "v2", "two_groups", "d64", "one_token", "sharp"])
+def test_attend_value_layouts_and_edges(tq, case):
+    cfg = workloads.CONFIGS["decode3b"]
+    n, G, scale, d = 300, 4, 1.0 / np.sqrt(cfg.d), cfg.d
+    chan = None
+    groups = [(cfg.d, 3)]
+    if case == "v1":
+        groups = [(cfg.d, 1)]
+    elif case == "v2":
+        groups = [(cfg.d, 2)]
+    elif case == "two_groups":
+        lcfg = workloads.CONFIGS["longctx"]
+        chan = workloads.group_channels(lcfg)
+        groups = [(32, 3), (96, 2)]
+    elif case == "d64":
+        d, groups = 64, [(64, 3)]
+    elif case == "one_token":
+        n, G = 1, 3
+    elif case == "sharp":
+        scale = 2.0      # nearly one-hot weights
+    say(f"attend {case}: n={n} G={G} groups={groups} d_v={d}")
+    kgpu, korc = both_params(cfg, 3)
+    vgpu, vorc = value_params(tq, cfg, groups, chan, d=d)
+    kb = _encode_banks(korc, workloads.keys(cfg, n=n, banks=[1]))
+    vb = _encode_banks(vorc, workloads.values(cfg, n=n, banks=[1], d=d))
+    q = workloads.queries(cfg, banks=[1], G=G)
+    say("max err", _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, scale, n))
+
+
+def test_attend_equal_logits_is_the_mean_value(tq):
+    """Zero keys give logit 0 for every token: the output is the mean decoded value."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode3b"]
+    n = 1500
+    kgpu, korc = both_params(cfg, 4)
+    vgpu, vorc = value_params(tq, cfg, [(cfg.d, 3)])
+    kb = _encode_banks(korc, np.zeros((1, n, cfg.d), np.float32))
+    vb = _encode_banks(vorc, workloads.values(cfg, n=n, banks=[0]))
+    kbank = upload_bank(tq, kgpu, kb[0], kb[1], kb[2], n)
+    vbank = upload_bank(tq, vgpu, vb[0], vb[1], vb[2], n)
+    q = torch.from_numpy(workloads.queries(cfg, banks=[0], G=5)).cuda()
+    out = tq.tq_attend(kgpu, kbank, vgpu, vbank, q, 0.1).cpu().numpy()[0]
+    v = oracle.decode(vorc, vb[0][0], vb[1][0], n)
+    mean = v.mean(axis=0)
+    tol = 1e-6 * (np.abs(v).mean(axis=0) + np.sqrt((v ** 2).mean()))
+    assert (np.abs(out - mean[None]) <= tol[None]).all()
+
+
+def test_attend_full_decode8b_layer_sampled(tq):
+    """One full 8B-class layer (64 banks x 32768 tokens, G = 4) on random bank bytes for
+    keys and values, in the launch configuration the benchmark uses; three banks checked
+    against the oracle."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    n = cfg.tokens
+    say("attend full decode8b layer, random banks")
+    kgpu, korc = both_params(cfg, 4)
+    vgpu, vorc = value_params(tq, cfg, [(cfg.d, 3)])
+    kW, npad, _ = kgpu.layout(n)
+    vW, _, _ = vgpu.layout(n)
+    kb = workloads.random_bank(cfg.cfg_id, cfg.banks, npad, kW, 1, layer=0)
+    vbits, vnorms, vr = workloads.random_bank(cfg.cfg_id, cfg.banks, npad, vW, 1, layer=1)
+    vb = (vbits, vnorms, np.zeros_like(vr))
+    q = workloads.queries(cfg)
+    say("max err", _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, 1.0 / np.sqrt(cfg.d), n,
+                                banks_to_check=[0, 37, 63]))

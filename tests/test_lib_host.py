@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol(tq):
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     lib = ctypes.CDLL(tq.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -137,10 +137,15 @@ def test_argument_validation_returns_before_any_launch(tq):
                 setattr(p.struct, k, v)
         return p
 
-    for p in [patched(d=100, group_dim=100), patched(m=100), patched(m=0), patched(group_bits=4),
+    for p in [patched(d=100, group_dim=100), patched(m=100), patched(m=16), patched(group_bits=4),
               patched(group_bits=0), patched(group_dim=64), patched(n_groups=3), patched(d=2048, group_dim=2048)]:
         assert L.tq_encode(p.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
         assert L.tq_score(p.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 1 << 20, None) == tq.TQ_ERR_ARG
+    # m = 0 (codes and norms only) is a valid encoding but has no estimator
+    mse_only = patched(m=0)
+    assert L.tq_bank_layout(mse_only.ref, 10, None, None, None) == tq.TQ_OK
+    assert L.tq_score(mse_only.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 1 << 20,
+                      None) == tq.TQ_ERR_UNSUPPORTED
     # missing matrices
     p = _params(tq)
     assert L.tq_bank_layout(p.ref, 10, None, None, None) == tq.TQ_ERR_ARG
@@ -192,6 +197,34 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 2, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
     assert L.tq_fp32_logits(None, 1, 10, 128, 0x1000, 4, 0x2000, None) == tq.TQ_ERR_ARG
     assert L.tq_copy(0x1001, 0x2000, 64, None) == tq.TQ_ERR_ARG
+    # decompression and attention: value params are MSE-only (m = 0), d_v <= 128
+    vals = patched(m=0)
+    D, At = L.tq_decode, L.tq_attend
+    assert D(good.ref, ctypes.byref(nullbank), 1, 10, 0x7000, None) == tq.TQ_ERR_ARG
+    assert D(good.ref, ctypes.byref(bank), 1, 10, None, None) == tq.TQ_ERR_ARG
+    assert D(good.ref, ctypes.byref(bank), -1, 10, 0x7000, None) == tq.TQ_ERR_ARG
+    assert D(patched(m=16).ref, ctypes.byref(bank), 1, 10, 0x7000, None) == tq.TQ_ERR_ARG
+    assert D(vals.ref, ctypes.byref(nullbank), 0, 10, None, None) == tq.TQ_OK
+    assert D(vals.ref, ctypes.byref(nullbank), 3, 0, None, None) == tq.TQ_OK
+    kb, vb = ctypes.byref(bank), ctypes.byref(tq.tq_bank(0x60000, 0x70000, None))
+    need = good.workspace_bytes(tq.TQ_OP_ATTEND, 2, 100, 4)
+    assert need > good.workspace_bytes(tq.TQ_OP_SCORE, 2, 100, 4) and need % 256 == 0
+    assert vals.workspace_bytes(tq.TQ_OP_ATTEND, 2, 100, 4) == 0  # no estimator for the logits
+    assert good.workspace_bytes(tq.TQ_OP_ATTEND, 2, 0, 4) == 0
+    def att(kp=good, keys=kb, vp=vals, values=vb, banks=2, n=100, q=0x1000, G=4, scale=0.125, out=0x8000,
+            ws=0x100000, ws_bytes=need):
+        return At(kp.ref, keys, vp.ref, values, banks, n, q, G, scale, out, ws, ws_bytes, None)
+    assert att(kp=vals) == tq.TQ_ERR_UNSUPPORTED
+    assert att(vp=patched(m=16)) == tq.TQ_ERR_ARG
+    assert att(vp=_with_fake_ptrs(tq, d=256, m=0, groups=((256, 2),))) == tq.TQ_ERR_UNSUPPORTED
+    assert att(n=0) == tq.TQ_ERR_ARG and att(G=0) == tq.TQ_ERR_ARG and att(banks=-1) == tq.TQ_ERR_ARG
+    assert att(scale=float("inf")) == tq.TQ_ERR_ARG
+    assert att(q=None) == tq.TQ_ERR_ARG and att(out=None) == tq.TQ_ERR_ARG
+    assert att(values=ctypes.byref(nullbank)) == tq.TQ_ERR_ARG
+    assert att(ws=None) == tq.TQ_ERR_WORKSPACE and att(ws=0x100010) == tq.TQ_ERR_WORKSPACE
+    assert att(ws_bytes=need - 256) == tq.TQ_ERR_WORKSPACE
+    assert att(banks=0, keys=ctypes.byref(nullbank), values=ctypes.byref(nullbank), q=None, out=None, ws=None,
+               ws_bytes=0) == tq.TQ_OK
     # empty inputs are valid no-ops
     assert L.tq_encode(good.ref, None, 0, 0, 10, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
     assert L.tq_encode(good.ref, None, 0, 3, 0, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK

@@ -539,6 +539,87 @@ def test_mse_only_one_bit_shrinks_inner_products_by_two_over_pi():
 
 
 # ------------------------------------------------------------------------------------
+# decode attention: softmax of the estimated logits over MSE-decoded values
+# ------------------------------------------------------------------------------------
+
+def _attend_setup(n, G, seed, kbits=2, vbits=3, key_scale=1.0):
+    g = np.random.default_rng(seed)
+    d = 64
+    kspec = oracle.Spec(d, d, [(d, kbits)])
+    vspec = oracle.Spec(d, 0, [(d, vbits)])
+    kprm = oracle.Params(kspec, [g.standard_normal((d, d)).astype(np.float32)],
+                         g.standard_normal((d, d)).astype(np.float32))
+    vprm = oracle.Params(vspec, [g.standard_normal((d, d)).astype(np.float32)], None)
+    keys = (key_scale * g.standard_normal((n, d))).astype(np.float32)
+    vals = g.standard_normal((n, d)).astype(np.float32)
+    q = g.standard_normal((G, d)).astype(np.float32)
+    return kprm, vprm, oracle.encode(kprm, keys), oracle.encode(vprm, vals), q
+
+
+def test_attend_over_equal_logits_is_the_mean_decoded_value():
+    """Zero keys give estimate 0 for every token (zero norms), and a zero scale flattens
+    any logits: either way the softmax is uniform and attention is the plain mean."""
+    kprm, vprm, kb, vb, q = _attend_setup(37, 3, 1)
+    n = 37
+    mean = oracle.decode(vprm, vb[0], vb[1], n).mean(axis=0)
+    out0 = oracle.attend(kprm, kb, vprm, vb, n, q, 0.0)
+    np.testing.assert_allclose(out0, np.repeat(mean[None], 3, axis=0), rtol=1e-13, atol=1e-15)
+    zb = oracle.encode(kprm, np.zeros((n, 64), np.float32))
+    out1 = oracle.attend(kprm, zb, vprm, vb, n, q, 0.125)
+    np.testing.assert_allclose(out1, np.repeat(mean[None], 3, axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_attend_over_two_tokens_is_the_logistic_blend():
+    """Two tokens: the softmax weight of the first is 1 / (1 + e^(scale (s2 - s1)))."""
+    kprm, vprm, kb, vb, q = _attend_setup(2, 4, 2)
+    s = oracle.score(kprm, kb[0], kb[1], kb[2], 2, q)
+    v = oracle.decode(vprm, vb[0], vb[1], 2)
+    scale = 0.3
+    w1 = 1.0 / (1.0 + np.exp(scale * (s[:, 1] - s[:, 0])))
+    expect = w1[:, None] * v[0][None] + (1.0 - w1)[:, None] * v[1][None]
+    np.testing.assert_allclose(oracle.attend(kprm, kb, vprm, vb, 2, q, scale), expect, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_with_one_dominant_logit_returns_that_value():
+    """One key far along the query direction takes all the weight."""
+    g = np.random.default_rng(3)
+    kprm, vprm, _, vb, q = _attend_setup(50, 1, 3)
+    keys = (0.1 * g.standard_normal((50, 64))).astype(np.float32)
+    keys[17] = 40.0 * q[0] / np.linalg.norm(q[0])
+    kb = oracle.encode(kprm, keys)
+    out = oracle.attend(kprm, kb, vprm, vb, 50, q, 1.0)
+    v17 = oracle.decode(vprm, vb[0], vb[1], 50)[17]
+    np.testing.assert_allclose(out[0], v17, rtol=0, atol=1e-9 * np.abs(v17).max())
+
+
+def test_attend_over_one_repeated_value_returns_it():
+    """A convex combination of copies of one vector is that vector, whatever the logits."""
+    g = np.random.default_rng(4)
+    kprm, vprm, kb, _, q = _attend_setup(40, 5, 4, key_scale=3.0)
+    x = g.standard_normal(64).astype(np.float32)
+    vb = oracle.encode(vprm, np.repeat(x[None], 40, axis=0))
+    xhat = oracle.decode(vprm, vb[0], vb[1], 1)[0]
+    out = oracle.attend(kprm, kb, vprm, vb, 40, q, 0.7)
+    np.testing.assert_allclose(out, np.repeat(xhat[None], 5, axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_attend_is_a_convex_combination_of_the_decoded_values():
+    """Every output coordinate lies between the smallest and largest decoded value, and
+    with n = d tokens whose decoded values are linearly independent the weights can be
+    recovered from the output: they sum to one and their log-ratios are the scaled logit
+    differences (the softmax's defining property)."""
+    kprm, vprm, kb, vb, q = _attend_setup(64, 2, 5)
+    v = oracle.decode(vprm, vb[0], vb[1], 64)
+    out = oracle.attend(kprm, kb, vprm, vb, 64, q, 0.5)
+    assert (out >= v.min(axis=0) - 1e-12).all() and (out <= v.max(axis=0) + 1e-12).all()
+    # recover the weights: out = p @ v with v square and invertible
+    p = np.linalg.solve(v.T, out.T).T
+    s = oracle.score(kprm, kb[0], kb[1], kb[2], 64, q)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(np.log(p[:, 1:] / p[:, :1]), 0.5 * (s[:, 1:] - s[:, :1]), rtol=0, atol=1e-4)
+
+
+# ------------------------------------------------------------------------------------
 # top-k
 # ------------------------------------------------------------------------------------
 

@@ -9,7 +9,8 @@ workload can be regenerated piecewise (one layer, one bank) without drawing
 the whole thing. Roles:
 
     1 keys, 2 queries, 3 rotation Gaussians, 4 projection S,
-    5 outlier-channel choice, 6 per-channel scales, 7 random banks
+    5 outlier-channel choice, 6 per-channel scales, 7 random banks,
+    8 values, 9 the value quantiser's rotation Gaussians
 
 Workload shapes follow the problem statements of the source pages: KV-cache
 keys of decode-time attention (batch, kv_head, token, head_dim) with GQA
@@ -26,6 +27,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 ROLE_KEYS, ROLE_QUERIES, ROLE_ROT, ROLE_PROJ, ROLE_CHAN, ROLE_SCALE, ROLE_BANK = 1, 2, 3, 4, 5, 6, 7
+ROLE_VALUES, ROLE_VROT = 8, 9
 
 
 @dataclasses.dataclass(frozen=True)
@@ -182,6 +184,27 @@ def queries(cfg: Config, layer: int = 0, banks: Optional[Sequence[int]] = None, 
             q /= np.linalg.norm(q.astype(np.float64), axis=1, keepdims=True).astype(np.float32)
         out[i] = q
     return out
+
+
+def values(cfg: Config, layer: int = 0, n: Optional[int] = None, banks: Optional[Sequence[int]] = None,
+           d: Optional[int] = None) -> np.ndarray:
+    """Values [len(banks), n, d] float32, i.i.d. N(0,1) (rounded to bf16 when the config
+    stores bf16 keys): the tokens' value vectors of a decode-time KV cache, stored next to
+    the keys by the MSE-only quantiser. Bank index as for :func:`keys`."""
+    n = cfg.tokens if n is None else n
+    d = cfg.d if d is None else d
+    banks = list(range(cfg.banks)) if banks is None else list(banks)
+    out = np.empty((len(banks), n, d), dtype=np.float32)
+    for i, b in enumerate(banks):
+        x = rng(cfg.cfg_id, ROLE_VALUES, layer * 100_000 + b).standard_normal((n, d), dtype=np.float32)
+        out[i] = _round_bf16(x) if cfg.key_dtype == "bf16" else x
+    return out
+
+
+def value_rotation_gaussians(cfg_id: int, dims: Sequence[int], layer: int = 0) -> List[np.ndarray]:
+    """As :func:`rotation_gaussians`, for the value quantiser's own rotation."""
+    g = rng(cfg_id, ROLE_VROT, layer)
+    return [g.standard_normal((dg, dg)).astype(np.float32) for dg in dims]
 
 
 def keys_device(cfg: Config, layer: int, device, n: Optional[int] = None, dtype=None):
