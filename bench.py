@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -374,6 +375,73 @@ def variants_extra(tq, device):
                                               tq.tq_make_codebook(groups[0][1])[2]]}
 
 
+def attend_extra(tq, device, layers=4, reps=12):
+    """Decode attention over decode8b layers (64 banks x 32768 tokens, G = 4): keys at b=4
+    (3-bit codebook + sketch), values MSE-only at 3 bits; `layers` distinct layers cycled so
+    that no layer's banks stay in the last-level cache. Per layer: the logits (tq_score), the
+    chunk kernel (softmax weights and the integer product with the value planes) and the
+    combine kernel."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    kprm = params_for(tq, cfg, 4, device)
+    vprm = tq.make_params(cfg.d, 0, [(cfg.d, 3)], workloads.value_rotation_gaussians(cfg.cfg_id, [cfg.d]), None,
+                          None, device)
+    kws = torch.empty(kprm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), dtype=torch.uint8, device=device)
+    vws = torch.empty(max(vprm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), 256), dtype=torch.uint8,
+                      device=device)
+    kb, vb, qs = [], [], []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    venc_ms = 0.0
+    for layer in range(layers):
+        kb.append(tq.tq_encode(kprm, workloads.keys_device(cfg, layer, device), tq.Bank(kprm, cfg.banks, cfg.tokens,
+                                                                                        device), workspace=kws))
+        vals = workloads.values_device(cfg, layer, device)
+        vbank = tq.Bank(vprm, cfg.banks, cfg.tokens, device)
+        tq.tq_encode(vprm, vals, vbank, workspace=vws)
+        a.record()
+        tq.tq_encode(vprm, vals, vbank, workspace=vws)
+        b.record()
+        torch.cuda.synchronize()
+        venc_ms += a.elapsed_time(b)
+        vb.append(vbank)
+        qs.append(workloads.queries_device(cfg, layer, device))
+        del vals
+    out = torch.empty((cfg.banks, cfg.G, cfg.d), dtype=torch.float32, device=device)
+    ws = tq.attend_workspace(kprm, kb[0], cfg.G)
+    scale = 1.0 / math.sqrt(cfg.d)
+    scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+    sws = tq.score_workspace(kprm, kb[0], cfg.G)
+
+    def run(fn):
+        for i in range(layers):
+            fn(i)
+        a.record()
+        for i in range(reps):
+            fn(i % layers)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    att_us = run(lambda i: tq.tq_attend(kprm, kb[i], vprm, vb[i], qs[i], scale, out=out, workspace=ws))
+    sc_us = run(lambda i: tq.tq_score(kprm, kb[i], qs[i], scores=scores, workspace=sws))
+    _, npad, kbpk = kprm.layout(cfg.tokens)
+    _, _, vbpk = vprm.layout(cfg.tokens)
+    n = cfg.banks * cfg.tokens
+    logit_bytes = 4 * cfg.G * n
+    return {
+        "workload": "decode8b attention, 64 banks x 32768 tokens, G=4, keys b=4 (m=128), values MSE-only 3-bit, "
+                    f"{layers} layers cycled",
+        "us_per_layer": att_us,
+        "logits_us_per_layer": sc_us,
+        "softmax_and_values_us_per_layer": att_us - sc_us,
+        "bytes_per_token": {"key": kbpk, "value": vbpk - 4, "logits_written_and_read": 2 * 4 * cfg.G},
+        "gbps_whole_call": (n * (kbpk + vbpk - 4) + 2 * logit_bytes) / (att_us * 1e-6) / 1e9,
+        "value_encode_keys_per_s": n / (venc_ms / layers * 1e-3),
+    }
+
+
 def search_extra(tq, device):
     """Vector search: 2,000,000 x 768 unit vectors, 1024 queries, top-10 per query, at
     b=4 and b=2; encode rate, top-k rate and recall@10 against the exact inner products."""
@@ -556,6 +624,9 @@ def main():
         out["search"] = search_extra(tq, device)
         log("streaming append")
         out["append"] = append_extra(tq, device)
+        torch.cuda.empty_cache()
+        log("decode attention")
+        out["attend"] = attend_extra(tq, device)
         torch.cuda.empty_cache()
         log("rotation / codebook variants")
         out["variants"] = variants_extra(tq, device)

@@ -35,7 +35,7 @@
  *          bucket index of rotated coordinate 32k+t of group g); then m/32 sign
  *          words (word k, bit t = [row 32k+t of S times the residual >= 0]).
  *   norms  (float)  [banks][n_pad][n_groups]: |x_g| per group.
- *   rnorms (float)  [banks][n_pad]: |residual|.
+ *   rnorms (float)  [banks][n_pad]: |residual| (0 for the MSE-only quantiser, m = 0).
  *   Slots n..n_pad-1 hold the encoding of the zero vector.
  */
 #ifndef TQ_H
@@ -137,7 +137,8 @@ int tq_make_rotation(int d, const float *gauss, float *rot);
 int tq_bank_layout(const tq_params *p, int64_t n, int64_t *words_per_key, int64_t *n_pad, int64_t *bytes_per_key);
 
 /* Device workspace bytes needed by `op` (a tq_op) for these sizes; 0 on bad
- * arguments. Pass at least this much, 256-byte aligned, to the call. */
+ * arguments. Pass at least this much, 256-byte aligned, to the call. An encode of an
+ * MSE-only layout (m = 0) with d <= 128 needs none (workspace may then be NULL). */
 size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, int32_t G, int32_t k);
 
 /* Encode (stages 1 and 2) keys (device) [banks][n][d] of dtype TQ_F32 or TQ_BF16
@@ -216,7 +217,7 @@ int tq_decode(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, f
  * [banks][G][kp->d], out (device) float32 [banks][G][d_v]. n >= 1, finite scale, else
  * TQ_ERR_ARG. The logits are formed into `workspace` (device) of
  * tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0) bytes, 256-byte aligned
- * (TQ_ERR_WORKSPACE otherwise), then reduced per chunk of 1024 tokens (softmax weights in
+ * (TQ_ERR_WORKSPACE otherwise), then reduced per chunk of 512 tokens (softmax weights in
  * 30-bit fixed point, exact integer products) and merged in fp64. */
 int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_params *vp, const tq_bank *values, int64_t banks,
               int64_t n, const float *q, int32_t G, float scale, float *out, void *workspace, size_t ws_bytes,

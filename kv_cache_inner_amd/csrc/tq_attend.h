@@ -30,8 +30,9 @@ namespace tq {
 
 constexpr int AT_THREADS = 256;                // four waves
 constexpr int AT_STEP = 64;                    // keys per product: four 16-key tiles
-constexpr int AT_CHUNK = 1024;                 // keys per work-group
+constexpr int AT_CHUNK = 512;                  // keys per work-group
 constexpr int AT_STEPS = AT_CHUNK / AT_STEP;
+constexpr int AT_RPL = AT_CHUNK / 256;         // weights per lane and key of a quad: keys 256 r + 4 lane + k
 constexpr int AT_DMAX = 128;                   // value dimension: one 32-coordinate word per wave
 
 struct AttnArgs {
@@ -54,10 +55,13 @@ __device__ __forceinline__ double at_wave_sum(double v) {
     return v;
 }
 
-__device__ __forceinline__ uint64_t at_wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// x of lane (i + N) mod 16 within each row of 16 lanes (DPP row rotation), fp64
+template <int N>
+__device__ __forceinline__ double at_row_ror(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x120 + N, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x120 + N, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // 4 x 4 byte transpose: out[b] byte k = in[k] byte b.
@@ -74,19 +78,34 @@ __device__ __forceinline__ u32x4 at_transpose_bytes(u32x4 x) {
     return y;
 }
 
+typedef __attribute__((address_space(3))) void at_lds_void;
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int AT_WAIT_VM0 = (7 << 4) | (15 << 8);
+
 // Partial attention of one chunk of AT_CHUNK keys for four queries of one bank.
 // grid (banks * chunks, ceil(G / 4)), AT_THREADS threads. Wave q computes the weights of
 // query 4 * blockIdx.y + q; wave w accumulates coordinate word w (32 coordinates, group
 // order) for the four queries.
-// part [bank][G][chunks][2 + d] floats: scaled maximum, sum of e^(z - max), then o_rot
-// (un-normalised, relative to that maximum).
+// part [bank][G][chunks][2 + d] floats: maximum of z = log2(e) scale logit, sum of
+// 2^(z - max), then o_rot (un-normalised, relative to that maximum).
+//
+// Memory: at entry every wave issues direct-to-LDS loads (global_load_lds_dwordx4) of its
+// word's stored planes for all tiles of the chunk, then the logits and norms of its
+// query; one wait covers them all, so a work-group costs one memory round trip and the
+// products run from LDS.
+template <int NG>
 __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     const float *__restrict__ scores, const uint32_t *__restrict__ vbits, const float *__restrict__ vnorms, long n,
     int n_tiles, int G, int chunks, float scale, AttnArgs a, float *__restrict__ part) {
-    __shared__ __align__(16) uint8_t s_a[2][16][AT_CHUNK];     // [group][row 4q + limb][key]: weight limbs
-    __shared__ __align__(16) uint32_t s_b[4][16][AT_STEP / 4];  // [wave][column 4P + byte][4 keys]
-    __shared__ int s_F[2][4];
-    __shared__ double s_vsum[2][4];
+    constexpr int TILES = AT_CHUNK / 16;
+    __shared__ __align__(16) uint32_t s_v[4][TILES * 3][16];    // [wave][tile * planes + p][key]: stored words
+    // rows padded by 16 bytes (s_a) and 4 dwords (s_b): the operand reads and the staging
+    // writes then spread over all LDS banks
+    __shared__ __align__(16) uint8_t s_a[NG][16][AT_CHUNK + 16];     // [group][row 4q + limb][key]: limbs
+    __shared__ __align__(16) uint32_t s_b[4][16][AT_STEP / 4 + 4];  // [wave][column 4P + byte][4 keys]
+    __shared__ int s_F[NG][4];
+    __shared__ double s_vsum[NG][4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,170 +115,253 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     const long k0 = (long)ch * AT_CHUNK;
     const long n_pad = (long)n_tiles * 16;
     const int PS = 2 + a.d;
+    const int t_first = (int)(k0 >> 4);
 
-    // ---- 1. weights of query q0 + wv for every key of the chunk (lane = key within a step)
+    // ---- 0. this wave's coordinate word: group, planes, and the direct loads of its planes
+    const int nwords = a.d >> 5;
+    const bool wlive = wv < nwords;
+    const int g = (NG > 1 && 32 * wv >= a.gdim[0]) ? 1 : 0;
+    const int gb = a.gbits[g];
+    const int pstride = a.gdim[g] >> 5;
+    const int wbase = a.gword[g] + wv - (a.goff[g] >> 5);
+    const uint32_t *vb = vbits + (size_t)bank * n_tiles * a.W * 16;
+    if (wlive) {
+        // rows tile * gb + p of 64 bytes (16 keys x one word), sixteen rows per load; tiles
+        // past the bank's end re-read its last tile (their keys carry zero weight)
+        for (int i = 0; i < AT_RPL * gb; ++i) {
+            const int row = 16 * i + (lane >> 2);
+            const int tile = min(t_first + row / gb, n_tiles - 1), p = row % gb;
+            __builtin_amdgcn_global_load_lds(vb + ((size_t)tile * a.W + wbase + p * pstride) * 16 + 4 * (lane & 3),
+                                             (at_lds_void *)&s_v[wv][16 * i][0], 16, 0, 0);
+        }
+    }
+
+    // ---- 1. weights of query q0 + wv; lane: keys 256 r + 4 lane + (0..3) of the chunk.
+    // Exponents in base 2: z = log2(e) scale logit, e = 2^(z - max z) (v_exp_f32); the chunk
+    // maximum is stored in the same units.
     {
         const int qg = q0 + wv;
-        const bool qlive = qg < G;
-        const float *srow = scores + ((size_t)bank * G + (qlive ? qg : 0)) * n;
-        float e[AT_STEPS];
-        float mx = -INFINITY;
+        const bool qlive = qg < G;                       // wave-uniform
+        const int nk = (int)min((long)AT_CHUNK, n - k0);  // keys of this chunk, >= 1
+        const int nkp = (int)min((long)AT_CHUNK, n_pad - k0);
+        const float *sb = scores + ((size_t)bank * G + (qlive ? qg : 0)) * n + k0;
+        const float *nb = vnorms + ((size_t)bank * n_pad + k0) * NG;
+        // loads at clamped addresses, all issued before the first wait (no branch around a
+        // load: each would wait on its own)
+        f32x4 nv[AT_RPL][NG];  // norms of keys 4 lane .. 4 lane + 3 (groups interleaved per key)
 #pragma unroll
-        for (int s = 0; s < AT_STEPS; ++s) {
-            const long key = k0 + AT_STEP * s + lane;
-            e[s] = (qlive && key < n) ? scale * srow[key] : -INFINITY;
-            mx = fmaxf(mx, e[s]);
+        for (int r = 0; r < AT_RPL; ++r) {
+            const int kb = min(256 * r + 4 * lane, nkp - 4);
+#pragma unroll
+            for (int h = 0; h < NG; ++h) nv[r][h] = reinterpret_cast<const f32x4 *>(nb + kb * NG)[h];
+        }
+        float e[AT_RPL][4];
+#pragma unroll
+        for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) e[r][k] = sb[min(256 * r + 4 * lane + k, nk - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        const float c2 = scale * 1.4426950408889634f;
+        float mx = -INFINITY;
+        if (nk == AT_CHUNK) {
+#pragma unroll
+            for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    e[r][k] *= c2;
+                    mx = fmaxf(mx, e[r][k]);
+                }
+        } else {
+#pragma unroll
+            for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    e[r][k] = 256 * r + 4 * lane + k < nk ? e[r][k] * c2 : -INFINITY;
+                    mx = fmaxf(mx, e[r][k]);
+                }
         }
         mx = at_wave_max(mx);
         double esum = 0.0;
 #pragma unroll
-        for (int s = 0; s < AT_STEPS; ++s) {
-            e[s] = e[s] == -INFINITY ? 0.0f : expf(e[s] - mx);
-            esum += (double)e[s];
-        }
+        for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                e[r][k] = qlive ? __builtin_amdgcn_exp2f(e[r][k] - mx) : 0.0f;  // 2^-inf = 0
+                esum += (double)e[r][k];
+            }
         esum = at_wave_sum(esum);
         if (qlive && lane == 0) {
             float *pp = part + (((size_t)bank * G + qg) * chunks + ch) * PS;
             pp[0] = mx;
             pp[1] = (float)esum;
         }
-        for (int g = 0; g < a.ng; ++g) {
-            float w[AT_STEPS];
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            float w[AT_RPL][4];
             float wm = 0.0f;
 #pragma unroll
-            for (int s = 0; s < AT_STEPS; ++s) {
-                const long key = k0 + AT_STEP * s + lane;
-                const float nu = key < n ? vnorms[((size_t)bank * n_pad + key) * a.ng + g] : 0.0f;
-                w[s] = e[s] * nu;
-                wm = fmaxf(wm, w[s]);
-            }
+            for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // norm (key k, group gg) is float NG k + gg of the lane's block; e = 0 past n
+                    w[r][k] = e[r][k] * nv[r][(NG * k + gg) >> 2][(NG * k + gg) & 3];
+                    wm = fmaxf(wm, w[r][k]);
+                }
             wm = at_wave_max(wm);
             // fixed point: w 2^F < 2^30 for every weight of the chunk
             int E = 0;
             if (wm > 0.0f) frexpf(wm, &E);
             const int F = wm > 0.0f ? 30 - E : 0;
-            uint64_t vsum = 0;
+            double vsum = 0.0;  // exact: at most 2^40
 #pragma unroll
-            for (int s = 0; s < AT_STEPS; ++s) {
-                const uint32_t V = (uint32_t)__float2int_rn(ldexpf(w[s], F));
-                vsum += V;
-                // balanced base-256 digits: bytes of V + 0x80808080, each minus 128
-                const uint32_t L = (V + 0x80808080u) ^ 0x80808080u;
+            for (int r = 0; r < AT_RPL; ++r) {
+                u32x4 L;
 #pragma unroll
-                for (int l = 0; l < 4; ++l) s_a[g][4 * wv + l][AT_STEP * s + lane] = (uint8_t)(L >> (8 * l));
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t V = (uint32_t)__float2int_rn(ldexpf(w[r][k], F));
+                    vsum += (double)V;
+                    // balanced base-256 digits: bytes of V + 0x80808080, each minus 128
+                    L[k] = (V + 0x80808080u) ^ 0x80808080u;
+                }
+                // limb l of the four keys -> row 4 wv + l
+                const u32x4 y = at_transpose_bytes(L);
+#pragma unroll
+                for (int l = 0; l < 4; ++l)
+                    *reinterpret_cast<uint32_t *>(&s_a[gg][4 * wv + l][256 * r + 4 * lane]) = y[l];
             }
-            vsum = at_wave_sum_u64(vsum);
+            vsum = at_wave_sum(vsum);
             if (lane == 0) {
-                s_F[g][wv] = F;
-                s_vsum[g][wv] = (double)vsum;
+                s_F[gg][wv] = F;
+                s_vsum[gg][wv] = vsum;
             }
         }
     }
+    __builtin_amdgcn_s_waitcnt(AT_WAIT_VM0);  // this wave's planes are in LDS
     __syncthreads();
 
     // ---- 2. wave wv: coordinate word wv of the four queries
-    const int nwords = a.d >> 5;
-    if (wv >= nwords) return;
-    const int g = (a.ng > 1 && 32 * wv >= a.gdim[0]) ? 1 : 0;
-    const int gb = a.gbits[g];
-    const int wl = wv - (a.goff[g] >> 5);
-    const int pstride = a.gdim[g] >> 5;
-    const int wbase = a.gword[g] + wl;
-    // staging role of this lane: tile T of the step, keys 4 s4 .. 4 s4 + 3, plane P
-    const int T = lane >> 4, s4 = (lane >> 2) & 3, P = lane & 3;
-    const int t_first = (int)(k0 >> 4);
-    const uint32_t *vb = vbits + (size_t)bank * n_tiles * a.W * 16;
+    if (wlive) {
+        // staging role of this lane: tile T of the step, keys 4 s4 .. 4 s4 + 3, plane P; a
+        // stored plane P reads its row (and, for the XOR of three planes, the XOR plane reads
+        // planes 0, 1, 2); unused columns (coefficient 0) read plane 0
+        const int T = lane >> 4, s4 = (lane >> 2) & 3, P = lane & 3;
+        const int pa = P < gb ? P : 0;
+        const int pb = P < gb ? P : (P == 3 && gb == 3 ? 1 : 0);
+        const int pc = P < gb ? P : (P == 3 && gb == 3 ? 2 : 0);
 
-    // Every lane issues three loads a step, XORed only when the step is used (so the loads
-    // stay in flight across the products): a stored plane P loads its word three times
-    // (a ^ a ^ a = a), the XOR plane loads planes 0, 1, 2, and unused columns (coefficient
-    // 0) load plane 0. Tiles past the bank's end re-read its last tile: their keys carry
-    // zero weight.
-    const int pa = P < gb ? P : 0;
-    const int pb = P < gb ? P : (P == 3 && gb == 3 ? 1 : 0);
-    const int pc = P < gb ? P : (P == 3 && gb == 3 ? 2 : 0);
-    const size_t o0 = (size_t)(wbase + pa * pstride) * 16 + 4 * s4;
-    const size_t o1 = (size_t)(wbase + pb * pstride) * 16 + 4 * s4;
-    const size_t o2 = (size_t)(wbase + pc * pstride) * 16 + 4 * s4;
-    struct Planes {
-        u32x4 x0, x1, x2;
-    };
-    auto load_step = [&](int s) -> Planes {
-        const int tile = min(t_first + 4 * s + T, n_tiles - 1);
-        const uint32_t *tw = vb + (size_t)tile * a.W * 16;
-        Planes r;
-        r.x0 = *(const u32x4 *)(tw + o0);
-        r.x1 = *(const u32x4 *)(tw + o1);
-        r.x2 = *(const u32x4 *)(tw + o2);
-        return r;
-    };
-
-    i32x4 acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = i32x4{0, 0, 0, 0};
-    const int col = lane & 15, kg = lane >> 4;
-    Planes x = load_step(0);
-    for (int s = 0; s < AT_STEPS; ++s) {
-        const u32x4 y = at_transpose_bytes(x.x0 ^ x.x1 ^ x.x2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) s_b[wv][4 * P + b][4 * T + s4] = y[b];
-        const i8x16 A = *(const i8x16 *)&s_a[g][col][AT_STEP * s + 16 * kg];
-        const u32x4 B = *(const u32x4 *)&s_b[wv][col][4 * kg];
-        if (s + 1 < AT_STEPS) x = load_step(s + 1);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const u32x4 bt = B & (0x01010101u << t);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, __builtin_bit_cast(i8x16, bt), acc[t], 0, 0, 0);
+        i32x4 acc[8];
+    #pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = i32x4{0, 0, 0, 0};
+        const int col = lane & 15, kg = lane >> 4;
+        for (int s = 0; s < AT_STEPS; ++s) {
+            const int rt = (4 * s + T) * gb;
+            u32x4 x = *(const u32x4 *)&s_v[wv][rt + pa][4 * s4];
+            if (gb == 3) x ^= *(const u32x4 *)&s_v[wv][rt + pb][4 * s4] ^ *(const u32x4 *)&s_v[wv][rt + pc][4 * s4];
+            const u32x4 y = at_transpose_bytes(x);
+    #pragma unroll
+            for (int b = 0; b < 4; ++b) s_b[wv][4 * P + b][4 * T + s4] = y[b];
+            const i8x16 A = *(const i8x16 *)&s_a[g][col][AT_STEP * s + 16 * kg];
+            const u32x4 B = *(const u32x4 *)&s_b[wv][col][4 * kg];
+    #pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const u32x4 bt = B & (0x01010101u << t);
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, __builtin_bit_cast(i8x16, bt), acc[t], 0, 0, 0);
+            }
         }
-    }
 
-    // ---- 3. lane (query c, column 4P + b): recombine limbs, weight the planes, add them up
-    const int c = lane >> 4, Pc = col >> 2, bc = col & 3;
-    const double coef = Pc < 4 ? a.coef[g][Pc] : 0.0;
-    const int qg = q0 + c;
-    const double fscale = ldexp(a.inv_sqrt_d[g], -s_F[g][c]);
-    const double bterm = a.bias[g] * s_vsum[g][c];
-    float *prow = part + (((size_t)bank * G + (qg < G ? qg : 0)) * chunks + ch) * PS + 2;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int64_t v = (int64_t)acc[t][0] + ((int64_t)acc[t][1] << 8) + ((int64_t)acc[t][2] << 16) +
-                          ((int64_t)acc[t][3] << 24);
-        double xv = (double)v * coef * (t == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << t));
-        xv += __shfl_xor(xv, 4, 64);
-        xv += __shfl_xor(xv, 8, 64);
-        if (Pc == 0 && qg < G) prow[32 * wv + 8 * bc + t] = (float)((xv - bterm) * fscale);
+        // ---- 3. lane (query c, column 4P + b): recombine limbs, weight the planes, add them up
+        const int c = lane >> 4, Pc = col >> 2, bc = col & 3;
+        const double *cf = g ? a.coef[1] : a.coef[0];
+        const double coef = Pc == 0 ? cf[0] : (Pc == 1 ? cf[1] : (Pc == 2 ? cf[2] : cf[3]));
+        const int qg = q0 + c;
+        const double fscale = ldexp(a.inv_sqrt_d[g], -s_F[g][c]);
+        const double bterm = a.bias[g] * s_vsum[g][c];
+        float *prow = part + (((size_t)bank * G + (qg < G ? qg : 0)) * chunks + ch) * PS + 2;
+    #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // exact: |limb sum| <= AT_CHUNK * 128 * 128
+            const double v = fma((double)acc[t][3], 16777216.0,
+                                 fma((double)acc[t][2], 65536.0, fma((double)acc[t][1], 256.0, (double)acc[t][0])));
+            double xv = v * (coef * (t == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << t)));
+            xv += at_row_ror<8>(xv);  // the four planes of a byte sit in lanes 4P + b of a row
+            xv += at_row_ror<4>(xv);
+            if (Pc == 0 && qg < G) prow[32 * wv + 8 * bc + t] = (float)((xv - bterm) * fscale);
+        }
     }
 }
 
-// Merge of the chunks and the rotation back: one work-group per (bank, query), one thread
-// per output channel. out [bank][G][d] float32 in channel order.
-__global__ __launch_bounds__(AT_DMAX) void attn_combine_kernel(const float *__restrict__ part, int chunks,
-                                                               const float *__restrict__ rot,
-                                                               const int *__restrict__ chan, AttnArgs a,
-                                                               float *__restrict__ out) {
+// Merge of the chunks and the rotation back: one wave per (bank, query). Every global read
+// is issued before the first wait: the rotation R_g (direct-to-LDS), the chunk maxima and
+// weight sums, and the partial rows of the first 64 chunks (two coordinates per lane).
+// The chunk maxima (base-2 units) give factors 2^(max_c - max);
+// o_rot = sum_c factor_c o_rot_c / sum_c factor_c sum_c in fp64, and then
+// out[chan[off_g + k]] = sum_j R_g[j][k] o_rot[off_g + j]. out [bank][G][d] float32.
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ part, int chunks,
+                                                         const float *__restrict__ rot, const int *__restrict__ chan,
+                                                         AttnArgs a, float *__restrict__ out) {
+    __shared__ __align__(16) float s_R[AT_DMAX * AT_DMAX];
     __shared__ double s_o[AT_DMAX];
-    const int tid = threadIdx.x;
-    const int PS = 2 + a.d;
-    const float *pb = part + (size_t)blockIdx.x * chunks * PS;
-    double mx = -INFINITY;
-    for (int c = 0; c < chunks; ++c) mx = fmax(mx, (double)pb[(size_t)c * PS]);
-    double tot = 0.0, v = 0.0;
-    for (int c = 0; c < chunks; ++c) {
-        const double f = exp((double)pb[(size_t)c * PS] - mx);
-        tot += f * (double)pb[(size_t)c * PS + 1];
-        if (tid < a.d) v += f * (double)pb[(size_t)c * PS + 2 + tid];
+    const int lane = threadIdx.x, d = a.d, PS = 2 + d;
+    const float *pq = part + (size_t)blockIdx.x * chunks * PS;
+    // the rotation blocks, back to back: d_0^2 (+ d_1^2) floats, a multiple of 256
+    const int nR = a.gdim[0] * a.gdim[0] + (a.ng > 1 ? a.gdim[1] * a.gdim[1] : 0);
+    for (int i = 0; i < nR / 256; ++i)
+        __builtin_amdgcn_global_load_lds(rot + 256 * i + 4 * lane, (at_lds_void *)&s_R[256 * i], 16, 0, 0);
+    const int k0 = min(lane, d - 1), k1 = min(lane + 64, d - 1);  // clamped reads; results unused
+    float pv0[64], pv1[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const float *pr = pq + (size_t)min(i, chunks - 1) * PS + 2;
+        pv0[i] = pr[k0];
+        pv1[i] = pr[k1];
     }
-    if (tid < a.d) s_o[tid] = v / tot;
-    __syncthreads();
-    // o[chan[off_g + k]] = sum_j R_g[j][k] o_rot[off_g + j]
-    if (tid < a.d) {
-        const int g = (a.ng > 1 && tid >= a.gdim[0]) ? 1 : 0;
-        const int dg = a.gdim[g], off = a.goff[g], k = tid - off;
-        const float *R = rot + (g ? (size_t)a.gdim[0] * a.gdim[0] : 0);
+    const int c0 = min(lane, chunks - 1);
+    const float m0 = pq[(size_t)c0 * PS], e0 = pq[(size_t)c0 * PS + 1];
+    __builtin_amdgcn_sched_barrier(0);
+    float mx = lane < chunks ? m0 : -INFINITY;
+    for (int c = lane + 64; c < chunks; c += 64) mx = fmaxf(mx, pq[(size_t)c * PS]);
+    mx = at_wave_max(mx);
+    double tot = 0.0, v0 = 0.0, v1 = 0.0;
+    for (int cb = 0; cb < chunks; cb += 64) {
+        float f, e;
+        if (cb == 0) {
+            f = lane < chunks ? m0 : -INFINITY;
+            e = e0;
+        } else {
+            const int c = min(cb + lane, chunks - 1);
+            f = cb + lane < chunks ? pq[(size_t)c * PS] : -INFINITY;
+            e = pq[(size_t)c * PS + 1];
+#pragma unroll
+            for (int i = 0; i < 64; ++i) {
+                const float *pr = pq + (size_t)min(cb + i, chunks - 1) * PS + 2;
+                pv0[i] = pr[k0];
+                pv1[i] = pr[k1];
+            }
+        }
+        f = __builtin_amdgcn_exp2f(f - mx);  // 0 past the last chunk
+        tot += (double)f * (double)e;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            const double fi = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
+            v0 += fi * (double)pv0[i];
+            v1 += fi * (double)pv1[i];
+        }
+    }
+    tot = at_wave_sum(tot);
+    s_o[lane] = v0 / tot;
+    s_o[lane + 64] = v1 / tot;
+    __builtin_amdgcn_s_waitcnt(AT_WAIT_VM0);  // the rotation is in LDS
+    __builtin_amdgcn_s_barrier();
+    for (int h = 0; h < 2; ++h) {
+        const int k = lane + 64 * h;
+        if (k >= d) continue;
+        const bool g1 = a.ng > 1 && k >= a.gdim[0];
+        const int dg = g1 ? a.gdim[1] : a.gdim[0], off = g1 ? a.goff[1] : 0, kk = k - off;
+        const float *R = s_R + (g1 ? a.gdim[0] * a.gdim[0] : 0) + kk;
         double r = 0.0;
-        for (int j = 0; j < dg; ++j) r += (double)R[(size_t)j * dg + k] * s_o[off + j];
-        const int cc = chan ? chan[tid] : tid;
-        out[(size_t)blockIdx.x * a.d + cc] = (float)r;
+#pragma unroll 16
+        for (int j = 0; j < dg; ++j) r += (double)R[j * dg] * s_o[off + j];
+        out[(size_t)blockIdx.x * d + (chan ? chan[k] : k)] = (float)r;
     }
 }
 

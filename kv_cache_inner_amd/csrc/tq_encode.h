@@ -216,7 +216,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
         }
         s = wave_sum_f64(s);
         const long sl = slot_of(i);
-        if (lane == 0 && sl >= 0) rnorms[(size_t)bank * out_pad + sl] = (float)sqrt(s);
+        // the MSE-only quantiser (m = 0) stores no residual norm: 0
+        if (lane == 0 && sl >= 0) rnorms[(size_t)bank * out_pad + sl] = m > 0 ? (float)sqrt(s) : 0.0f;
     }
 
     // 4. stage 2 on MFMA: P = U S'^T, sign = [P >= 0]
@@ -737,7 +738,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
 #pragma unroll
                     for (int w = 0; w < ENCS_ROT; ++w) s += (double)s_rho[buf ^ 1][w][lane];
                     const long fs = out_slot(tp, lane);
-                    if (fs >= 0) rnorms[fs] = (float)sqrt(s);
+                    if (fs >= 0) rnorms[fs] = M > 0 ? (float)sqrt(s) : 0.0f;  // none stored for m = 0
                 }
                 // project tile tp's residual, add its sign words
                 if (prj_live) {

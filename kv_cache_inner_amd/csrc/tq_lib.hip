@@ -461,7 +461,7 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (banks == 0 || n == 0) return TQ_OK;
     if (!keys || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
     const EncWs ew = enc_ws_layout(p, banks, n);
-    if (!workspace || ws_bytes < ew.total || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
+    if (ew.total && (!workspace || ws_bytes < ew.total || ((uintptr_t)workspace & 255))) return TQ_ERR_WORKSPACE;
     if (p->m == 0 && enc_large(p)) return TQ_ERR_UNSUPPORTED;  // MSE-only keys up to 128 dimensions
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
@@ -552,8 +552,8 @@ extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype,
     if (flags & ~TQ_APPEND_PREPARED) return TQ_ERR_ARG;
     if (banks == 0 || count == 0 || n_cap == 0) return TQ_OK;
     if (!keys || !pos || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
-    if (!workspace || ws_bytes < enc_ws_layout(p, banks, count).total || ((uintptr_t)workspace & 255))
-        return TQ_ERR_WORKSPACE;
+    const size_t ws_need = enc_ws_layout(p, banks, count).total;
+    if (ws_need && (!workspace || ws_bytes < ws_need || ((uintptr_t)workspace & 255))) return TQ_ERR_WORKSPACE;
     const int64_t n_tiles = (count + 15) / 16, cap_tiles = (n_cap + 15) / 16;
     if (banks * n_tiles > INT32_MAX || cap_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     const size_t smem = enc_smem_bytes(p->d, p->m);
@@ -957,12 +957,16 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
         return rc;
     hipStream_t st = (hipStream_t)stream;
     const int64_t n_tiles = (n + 15) / 16;
-    hipLaunchKernelGGL(attn_chunk_kernel, dim3((unsigned)(banks * chunks), (unsigned)((G + 3) / 4)), dim3(AT_THREADS),
-                       0, st, logits, values->bits, values->norms, (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a,
-                       part);
+    const dim3 grid((unsigned)(banks * chunks), (unsigned)((G + 3) / 4));
+    if (vp->n_groups == 1)
+        hipLaunchKernelGGL(attn_chunk_kernel<1>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
+                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a, part);
+    else
+        hipLaunchKernelGGL(attn_chunk_kernel<2>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
+                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a, part);
     if ((rc = launch_status())) return rc;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(AT_DMAX), 0, st, part, (int)chunks,
-                       vp->rot, vp->group_chan, a, out);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(64), 0, st, part, (int)chunks, vp->rot,
+                       vp->group_chan, a, out);
     return launch_status();
 }
 

@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import both_params, check_scores, upload_bank
+from parity import both_params, check_encode, check_scores, download_bank, upload_bank
 
 pytestmark = pytest.mark.gpu
 
@@ -105,13 +105,43 @@ def _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, scale, n, banks_to_check
 
 
 # ------------------------------------------------------------------------------------------
+# MSE-only encoding (m = 0) of the values by the GPU encoder
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["bf16_b3", "f32_b2", "two_groups", "d64_unaligned"])
+def test_encode_mse_only_values(tq, case):
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    n, d, chan, groups, banks = 1000, cfg.d, None, [(cfg.d, 3)], [0, 7]
+    dtype = torch.bfloat16
+    if case == "f32_b2":
+        groups, dtype = [(cfg.d, 2)], torch.float32
+    elif case == "two_groups":
+        lcfg = workloads.CONFIGS["longctx"]
+        chan = workloads.group_channels(lcfg)
+        groups = [(32, 3), (96, 2)]
+    elif case == "d64_unaligned":
+        n, d, groups = 999, 64, [(64, 3)]
+    say(f"encode values m=0 {case}: n={n} d={d} groups={groups}")
+    gpu, orc = value_params(tq, cfg, groups, chan, d=d)
+    x = workloads.values(cfg, n=n, banks=banks, d=d)   # bf16-valued floats
+    bank = tq.Bank(gpu, len(banks), n)
+    tq.tq_encode(gpu, torch.from_numpy(x).cuda().to(dtype), bank)
+    torch.cuda.synchronize()
+    gb = download_bank(bank)
+    report = {}
+    for b in range(len(banks)):
+        check_encode((gb[0][b], gb[1][b], gb[2][b]), oracle.encode_trace(orc, x[b]), orc, n, report)
+    say("report", report)
+
+
+# ------------------------------------------------------------------------------------------
 # decompression
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("case", ["keys_b4", "values_b3", "values_b1", "two_groups", "d768"])
 def test_decode_matches_oracle(tq, case):
-    import dataclasses
-
     cfg = workloads.CONFIGS["decode8b"]
     n = 1000
     if case == "keys_b4":

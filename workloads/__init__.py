@@ -227,6 +227,20 @@ def keys_device(cfg: Config, layer: int, device, n: Optional[int] = None, dtype=
     return x.to(dtype)
 
 
+def values_device(cfg: Config, layer: int, device, n: Optional[int] = None, dtype=None):
+    """Full-size values drawn directly on a torch device: same distribution as
+    :func:`values`, torch's generator seeded with the values' seed."""
+    import torch
+
+    n = cfg.tokens if n is None else n
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_of(cfg.cfg_id, ROLE_VALUES, layer))
+    x = torch.randn((cfg.banks, n, cfg.d), generator=gen, device=device, dtype=torch.float32)
+    if dtype is None:
+        dtype = torch.bfloat16 if cfg.key_dtype == "bf16" else torch.float32
+    return x.to(dtype)
+
+
 def queries_device(cfg: Config, layer: int, device, G: Optional[int] = None):
     import torch
 
