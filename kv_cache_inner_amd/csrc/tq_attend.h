@@ -130,7 +130,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
         // past the bank's end re-read its last tile (their keys carry zero weight)
         for (int i = 0; i < AT_RPL * gb; ++i) {
             const int row = 16 * i + (lane >> 2);
-            const int tile = min(t_first + row / gb, n_tiles - 1), p = row % gb;
+            const int rt = gb == 1 ? row : (gb == 2 ? row >> 1 : (row * 43691) >> 17);  // row / gb
+            const int tile = min(t_first + rt, n_tiles - 1), p = row - rt * gb;
             __builtin_amdgcn_global_load_lds(vb + ((size_t)tile * a.W + wbase + p * pstride) * 16 + 4 * (lane & 3),
                                              (at_lds_void *)&s_v[wv][16 * i][0], 16, 0, 0);
         }
@@ -183,12 +184,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
         mx = at_wave_max(mx);
         double esum = 0.0;
 #pragma unroll
-        for (int r = 0; r < AT_RPL; ++r)
+        for (int r = 0; r < AT_RPL; ++r) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < 4; ++k)
                 e[r][k] = qlive ? __builtin_amdgcn_exp2f(e[r][k] - mx) : 0.0f;  // 2^-inf = 0
-                esum += (double)e[r][k];
-            }
+            // pairwise in fp32 (relative error <= 2^-23), then fp64
+            esum += (double)((e[r][0] + e[r][1]) + (e[r][2] + e[r][3]));
+        }
         esum = at_wave_sum(esum);
         if (qlive && lane == 0) {
             float *pp = part + (((size_t)bank * G + qg) * chunks + ch) * PS;
@@ -216,13 +218,14 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
 #pragma unroll
             for (int r = 0; r < AT_RPL; ++r) {
                 u32x4 L;
+                uint32_t V[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const uint32_t V = (uint32_t)__float2int_rn(ldexpf(w[r][k], F));
-                    vsum += (double)V;
+                    V[k] = (uint32_t)__float2int_rn(ldexpf(w[r][k], F));
                     // balanced base-256 digits: bytes of V + 0x80808080, each minus 128
-                    L[k] = (V + 0x80808080u) ^ 0x80808080u;
+                    L[k] = (V[k] + 0x80808080u) ^ 0x80808080u;
                 }
+                vsum += (double)(V[0] + V[1]) + (double)(V[2] + V[3]);  // pairs < 2^31: exact
                 // limb l of the four keys -> row 4 wv + l
                 const u32x4 y = at_transpose_bytes(L);
 #pragma unroll
