@@ -55,15 +55,6 @@ __device__ __forceinline__ double at_wave_sum(double v) {
     return v;
 }
 
-// x of lane (i + N) mod 16 within each row of 16 lanes (DPP row rotation), fp64
-template <int N>
-__device__ __forceinline__ double at_row_ror(double x) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x120 + N, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x120 + N, 0xF, 0xF, false);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
 // 4 x 4 byte transpose: out[b] byte k = in[k] byte b.
 __device__ __forceinline__ u32x4 at_transpose_bytes(u32x4 x) {
     const uint32_t t0 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
@@ -272,23 +263,33 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
             }
         }
 
-        // ---- 3. lane (query c, column 4P + b): recombine limbs, weight the planes, add them up
-        const int c = lane >> 4, Pc = col >> 2, bc = col & 3;
-        const double *cf = g ? a.coef[1] : a.coef[0];
-        const double coef = Pc == 0 ? cf[0] : (Pc == 1 ? cf[1] : (Pc == 2 ? cf[2] : cf[3]));
-        const int qg = q0 + c;
-        const double fscale = ldexp(a.inv_sqrt_d[g], -s_F[g][c]);
-        const double bterm = a.bias[g] * s_vsum[g][c];
-        float *prow = part + (((size_t)bank * G + (qg < G ? qg : 0)) * chunks + ch) * PS + 2;
-    #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            // exact: |limb sum| <= AT_CHUNK * 128 * 128
-            const double v = fma((double)acc[t][3], 16777216.0,
-                                 fma((double)acc[t][2], 65536.0, fma((double)acc[t][1], 256.0, (double)acc[t][0])));
-            double xv = v * (coef * (t == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << t)));
-            xv += at_row_ror<8>(xv);  // the four planes of a byte sit in lanes 4P + b of a row
-            xv += at_row_ror<4>(xv);
-            if (Pc == 0 && qg < G) prow[32 * wv + 8 * bc + t] = (float)((xv - bterm) * fscale);
+        // ---- 3. recombine: lane (query c, column 4P + b) turns its limb sums into one fp64
+        // plane term per shift t; through the wave's (now free) staging LDS, lane (c, b, t0)
+        // then adds the four planes of coordinates 8b + t0 and 8b + t0 + 4 and stores them
+        {
+            const int Pc = col >> 2;
+            const double *cf = g ? a.coef[1] : a.coef[0];
+            const double coef = Pc == 0 ? cf[0] : (Pc == 1 ? cf[1] : (Pc == 2 ? cf[2] : cf[3]));
+            double *so = reinterpret_cast<double *>(&s_v[wv][0][0]);  // [8][64], 4 KB of the wave's 6 KB
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                // exact: |limb sum| <= AT_CHUNK * 128 * 128
+                const double v = fma((double)acc[t][3], 16777216.0,
+                                     fma((double)acc[t][2], 65536.0, fma((double)acc[t][1], 256.0, (double)acc[t][0])));
+                so[64 * t + lane] = v * (coef * (t == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << t)));
+            }
+            const int c = lane >> 4, bc = (lane >> 2) & 3, t0 = lane & 3;
+            const int qg = q0 + c;
+            const double fscale = ldexp(a.inv_sqrt_d[g], -s_F[g][c]);
+            const double bterm = a.bias[g] * s_vsum[g][c];
+            float *prow = part + (((size_t)bank * G + (qg < G ? qg : 0)) * chunks + ch) * PS + 2 + 32 * wv + 8 * bc;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = t0 + 4 * h;
+                const double *r = so + 64 * t + 16 * c + bc;
+                const double xv = (r[0] + r[4]) + (r[8] + r[12]);  // planes 0..3 of (c, b)
+                if (qg < G) prow[t] = (float)((xv - bterm) * fscale);
+            }
         }
     }
 }
