@@ -210,18 +210,20 @@ int tq_decode(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, f
 
 /* Decode attention over a packed KV cache (same write-up, usage example: keys held by the
  * inner-product quantiser, values by the MSE quantiser): for bank b and query row g,
- *   out[b][g] = sum_i softmax_i(scale * est(q[b][g], key_i)) * x_hat(value_i),
- * est as tq_score returns it (fp32) and x_hat as tq_decode forms it. keys: a bank of n
- * tokens under kp (m > 0); values: a bank of the same n tokens under vp (any m; the sketch
- * is ignored), d_v = vp->d <= 128 (else TQ_ERR_UNSUPPORTED). q (device) float32
- * [banks][G][kp->d], out (device) float32 [banks][G][d_v]. n >= 1, finite scale, else
- * TQ_ERR_ARG. The logits are formed into `workspace` (device) of
- * tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0) bytes, 256-byte aligned
- * (TQ_ERR_WORKSPACE otherwise), then reduced per chunk of 512 tokens (softmax weights in
- * 30-bit fixed point, exact integer products) and merged in fp64. */
+ *   out[b][g] = sum_{i < len_b} softmax_i(scale * est(q[b][g], key_i)) * x_hat(value_i),
+ * est as tq_score returns it (fp32) and x_hat as tq_decode forms it. keys: banks of n slots
+ * under kp (m > 0); values: banks of the same n slots under vp (any m; the sketch is ignored),
+ * d_v = vp->d <= 128 (else TQ_ERR_UNSUPPORTED). lengths (device) int32[banks], nullable: bank
+ * b attends over its first len_b = min(max(lengths[b], 0), n) slots (a growing cache filled
+ * by tq_encode_append; slots past len_b may hold anything, NaN included); NULL = all n. A
+ * bank with len_b = 0 gets out = 0. q (device) float32 [banks][G][kp->d], out (device) float32
+ * [banks][G][d_v]. n >= 1, finite scale, else TQ_ERR_ARG. The logits of all n slots are formed
+ * into `workspace` (device) of tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0) bytes,
+ * 256-byte aligned (TQ_ERR_WORKSPACE otherwise), then reduced per chunk of 512 slots (softmax
+ * weights in 30-bit fixed point, exact integer products) and merged in fp64. */
 int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_params *vp, const tq_bank *values, int64_t banks,
-              int64_t n, const float *q, int32_t G, float scale, float *out, void *workspace, size_t ws_bytes,
-              void *stream);
+              int64_t n, const int32_t *lengths, const float *q, int32_t G, float scale, float *out, void *workspace,
+              size_t ws_bytes, void *stream);
 
 /* Measurement kernels (not part of the method):
  * fp32 logits against unquantized keys, scores[b][g][i] = q[b][g] . keys[b][i]

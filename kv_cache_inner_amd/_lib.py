@@ -68,7 +68,7 @@ def _load():
         "tq_score": (ctypes.c_int, [P, B, i64, i64, vp, i32, vp, vp, sz, vp]),
         "tq_topk": (ctypes.c_int, [P, B, i64, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
         "tq_decode": (ctypes.c_int, [P, B, i64, i64, vp, vp]),
-        "tq_attend": (ctypes.c_int, [P, B, P, B, i64, i64, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
+        "tq_attend": (ctypes.c_int, [P, B, P, B, i64, i64, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
         "tq_fp32_logits": (ctypes.c_int, [vp, i64, i64, i32, vp, i32, vp, vp]),
         "tq_copy": (ctypes.c_int, [vp, vp, sz, vp]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -320,21 +320,25 @@ def attend_workspace(kparams: Params, bank: Bank, G: int):
     return _workspace(kparams.workspace_bytes(TQ_OP_ATTEND, bank.banks, bank.n, G), bank.bits.device)
 
 
-def tq_attend(kparams: Params, kbank: Bank, vparams: Params, vbank: Bank, q, scale: float, out=None, workspace=None,
-              stream=None):
+def tq_attend(kparams: Params, kbank: Bank, vparams: Params, vbank: Bank, q, scale: float, lengths=None, out=None,
+              workspace=None, stream=None):
     """Decode attention: softmax(scale * estimated logits) over the tokens of each bank,
-    applied to the decompressed values. q [banks, G, d_k] -> out [banks, G, d_v]."""
+    applied to the decompressed values. q [banks, G, d_k] -> out [banks, G, d_v].
+    lengths: optional device int32 tensor [banks], the number of leading slots each bank
+    attends over (default: all kbank.n)."""
     import torch
 
     assert q.is_contiguous() and q.dim() == 3 and q.shape[0] == kbank.banks and q.shape[2] == kparams.d
     assert vbank.banks == kbank.banks and vbank.n == kbank.n
+    if lengths is not None:
+        assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.numel() == kbank.banks
     G = q.shape[1]
     if out is None:
         out = torch.empty((kbank.banks, G, vparams.d), dtype=torch.float32, device=q.device)
     ws = workspace if workspace is not None else attend_workspace(kparams, kbank, G)
     _check("tq_attend", _lib.tq_attend(kparams.ref, kbank.ref, vparams.ref, vbank.ref, kbank.banks, kbank.n,
-                                       q.data_ptr(), G, float(scale), out.data_ptr(), ws.data_ptr(), ws.numel(),
-                                       _stream(stream)))
+                                       _ptr(lengths), q.data_ptr(), G, float(scale), out.data_ptr(), ws.data_ptr(),
+                                       ws.numel(), _stream(stream)))
     return out
 
 

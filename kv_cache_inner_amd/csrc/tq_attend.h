@@ -88,7 +88,8 @@ constexpr int AT_WAIT_VM0 = (7 << 4) | (15 << 8);
 template <int NG>
 __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     const float *__restrict__ scores, const uint32_t *__restrict__ vbits, const float *__restrict__ vnorms, long n,
-    int n_tiles, int G, int chunks, float scale, AttnArgs a, float *__restrict__ part) {
+    int n_tiles, int G, int chunks, float scale, const int32_t *__restrict__ lengths, AttnArgs a,
+    float *__restrict__ part) {
     constexpr int TILES = AT_CHUNK / 16;
     __shared__ __align__(16) uint32_t s_v[4][TILES * 3][16];    // [wave][tile * planes + p][key]: stored words
     // rows padded by 16 bytes (s_a) and 4 dwords (s_b): the operand reads and the staging
@@ -134,8 +135,11 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     {
         const int qg = q0 + wv;
         const bool qlive = qg < G;                       // wave-uniform
-        const int nk = (int)min((long)AT_CHUNK, n - k0);  // keys of this chunk, >= 1
+        const int nk = (int)min((long)AT_CHUNK, n - k0);  // keys of this chunk in memory, >= 1
         const int nkp = (int)min((long)AT_CHUNK, n_pad - k0);
+        // keys that take part: the bank's first lengths[bank] (all n without lengths)
+        const long len = lengths ? min((long)max(lengths[bank], 0), n) : n;
+        const int nkv = (int)max(min((long)AT_CHUNK, len - k0), 0L);
         const float *sb = scores + ((size_t)bank * G + (qlive ? qg : 0)) * n + k0;
         const float *nb = vnorms + ((size_t)bank * n_pad + k0) * NG;
         // loads at clamped addresses, all issued before the first wait (no branch around a
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const float c2 = scale * 1.4426950408889634f;
         float mx = -INFINITY;
-        if (nk == AT_CHUNK) {
+        if (nkv == AT_CHUNK) {
 #pragma unroll
             for (int r = 0; r < AT_RPL; ++r)
 #pragma unroll
@@ -168,17 +172,18 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
             for (int r = 0; r < AT_RPL; ++r)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    e[r][k] = 256 * r + 4 * lane + k < nk ? e[r][k] * c2 : -INFINITY;
+                    e[r][k] = 256 * r + 4 * lane + k < nkv ? e[r][k] * c2 : -INFINITY;
                     mx = fmaxf(mx, e[r][k]);
                 }
         }
         mx = at_wave_max(mx);
+        const bool live = qlive && mx != -INFINITY;  // a query and at least one key
         double esum = 0.0;
 #pragma unroll
         for (int r = 0; r < AT_RPL; ++r) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                e[r][k] = qlive ? __builtin_amdgcn_exp2f(e[r][k] - mx) : 0.0f;  // 2^-inf = 0
+                e[r][k] = live ? __builtin_amdgcn_exp2f(e[r][k] - mx) : 0.0f;  // 2^-inf = 0
             // pairwise in fp32 (relative error <= 2^-23), then fp64
             esum += (double)((e[r][0] + e[r][1]) + (e[r][2] + e[r][3]));
         }
@@ -196,8 +201,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
             for (int r = 0; r < AT_RPL; ++r)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    // norm (key k, group gg) is float NG k + gg of the lane's block; e = 0 past n
-                    w[r][k] = e[r][k] * nv[r][(NG * k + gg) >> 2][(NG * k + gg) & 3];
+                    // norm (key k, group gg) is float NG k + gg of the lane's block; keys that
+                    // take no part have e = 0 and whatever their slot holds as norm
+                    const float nu = nv[r][(NG * k + gg) >> 2][(NG * k + gg) & 3];
+                    w[r][k] = e[r][k] > 0.0f ? e[r][k] * nu : 0.0f;
                     wm = fmaxf(wm, w[r][k]);
                 }
             wm = at_wave_max(wm);
@@ -352,8 +359,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restric
         }
     }
     tot = at_wave_sum(tot);
-    s_o[lane] = v0 / tot;
-    s_o[lane + 64] = v1 / tot;
+    if (mx == -INFINITY) tot = 0.0, v0 = v1 = 0.0;  // no key took part: the output is 0
+    s_o[lane] = tot > 0.0 ? v0 / tot : 0.0;
+    s_o[lane + 64] = tot > 0.0 ? v1 / tot : 0.0;
     __builtin_amdgcn_s_waitcnt(AT_WAIT_VM0);  // the rotation is in LDS
     __builtin_amdgcn_s_barrier();
     for (int h = 0; h < 2; ++h) {

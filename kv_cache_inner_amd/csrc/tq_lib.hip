@@ -930,8 +930,8 @@ static bool attn_args(const tq_params *p, AttnArgs *a) {
 }
 
 extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_params *vp, const tq_bank *values,
-                         int64_t banks, int64_t n, const float *q, int32_t G, float scale, float *out, void *workspace,
-                         size_t ws_bytes, void *stream) {
+                         int64_t banks, int64_t n, const int32_t *lengths, const float *q, int32_t G, float scale,
+                         float *out, void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(kp);
     if (rc) return rc;
     if ((rc = check_params(vp))) return rc;
@@ -960,10 +960,10 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
     const dim3 grid((unsigned)(banks * chunks), (unsigned)((G + 3) / 4));
     if (vp->n_groups == 1)
         hipLaunchKernelGGL(attn_chunk_kernel<1>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
-                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a, part);
+                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
     else
         hipLaunchKernelGGL(attn_chunk_kernel<2>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
-                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, a, part);
+                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(64), 0, st, part, (int)chunks, vp->rot,
                        vp->group_chan, a, out);

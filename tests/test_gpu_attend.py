@@ -259,3 +259,102 @@ def test_attend_full_decode8b_layer_sampled(tq):
     q = workloads.queries(cfg)
     say("max err", _attend_case(tq, kgpu, korc, vgpu, vorc, kb, vb, q, 1.0 / np.sqrt(cfg.d), n,
                                 banks_to_check=[0, 37, 63]))
+
+
+def test_attend_prefix_lengths_over_garbage_slots(tq):
+    """Banks of 1200 slots whose first 1102 hold oracle-encoded tokens and whose other slots
+    hold NaN norms and random bits; per-bank lengths pick the attended prefix: a partial last
+    chunk, exactly one chunk, one token, none (output 0), and one past n (clamped to n)."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    n_cap, n_fill, G = 1200, 1102, 4
+    lengths = [n_fill, 512, 1, 0, 700, 5000]
+    banks = len(lengths)
+    say(f"attend prefix lengths {lengths} over {n_cap} slots")
+    kgpu, korc = both_params(cfg, 4)
+    vgpu, vorc = value_params(tq, cfg, [(cfg.d, 3)])
+    bsel = list(range(banks))
+    kb = _encode_banks(korc, workloads.keys(cfg, n=n_fill, banks=bsel))
+    vb = _encode_banks(vorc, workloads.values(cfg, n=n_fill, banks=bsel))
+    g = np.random.default_rng(11)
+
+    def padded(prm, arrs):
+        W, npad, _ = prm.layout(n_cap)
+        bits = g.integers(0, 2**32, size=(banks, npad // 16, W, 16), dtype=np.uint64).astype(np.uint32)
+        norms = np.full((banks, npad, prm.ng), np.nan, np.float32)
+        rn = np.full((banks, npad), np.nan, np.float32)
+        t = arrs[0].shape[1]
+        bits[:, :t] = arrs[0]  # whole tiles of the filled part (its padding slots included)
+        norms[:, : t * 16] = arrs[1]
+        rn[:, : t * 16] = arrs[2]
+        # slots n_fill .. end of its tile: garbage as well
+        bits_flat = bits.transpose(0, 1, 3, 2).reshape(banks, -1, W)
+        bits_flat[:, n_fill:] = g.integers(0, 2**32, size=bits_flat[:, n_fill:].shape, dtype=np.uint64)
+        bits = bits_flat.reshape(banks, npad // 16, 16, W).transpose(0, 1, 3, 2).copy()
+        norms[:, n_fill:] = np.nan
+        rn[:, n_fill:] = np.nan
+        return upload_bank(tq, prm, bits, norms, rn, n_cap)
+
+    kbank, vbank = padded(kgpu, kb), padded(vgpu, vb)
+    q = workloads.queries(cfg, banks=bsel, G=G)
+    scale = 1.0 / np.sqrt(cfg.d)
+    out = tq.tq_attend(kgpu, kbank, vgpu, vbank, torch.from_numpy(q).cuda(), scale,
+                       lengths=torch.tensor(lengths, dtype=torch.int32, device="cuda")).cpu().numpy()
+    logits = tq.tq_score(kgpu, kbank, torch.from_numpy(q).cuda()).cpu().numpy()
+    assert np.isfinite(out).all()
+    for b, L in enumerate(lengths):
+        L = min(L, n_cap)
+        if L == 0:
+            assert (out[b] == 0).all()
+            continue
+        if L > n_fill:  # clamped to n: the garbage slots take part; only finiteness is checked
+            continue
+        s_ref = oracle.score(korc, kb[0][b], kb[1][b], kb[2][b], L, q[b])
+        e = check_scores(logits[b][:, :L], s_ref, f"logits bank {b}")
+        v = oracle.decode(vorc, vb[0][b], vb[1][b], L)
+        z = scale * s_ref
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ref = oracle.attend(korc, (kb[0][b], kb[1][b], kb[2][b]), vorc, (vb[0][b], vb[1][b], vb[2][b]), L, q[b], scale)
+        say(f"bank {b} len {L} max err", _check_attend(out[b], ref, v, p, e, scale, f"bank {b}"))
+
+
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_append_mse_only_values(tq, unaligned):
+    """A decode step's value appends: MSE-only (m = 0) values appended at per-bank slots by
+    tq_encode_append match the oracle's encoding; untouched slots keep their bytes."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    gpu, orc = value_params(tq, cfg, [(cfg.d, 3)])
+    n_cap, banks, count = 80, 2, 21
+    vals = workloads.values(cfg, n=count, banks=[4, 5])
+    bank = tq.Bank(gpu, banks, n_cap)
+    bank.bits.fill_(0x5A5A5A5A)
+    bank.norms.fill_(-1.0)
+    bank.rnorms.fill_(-2.0)
+    pos = np.array([3, 40], np.int64)
+    vv = torch.from_numpy(vals).cuda().to(torch.bfloat16)
+    if unaligned:
+        flat = torch.zeros(vv.numel() + 1, dtype=torch.bfloat16, device="cuda")
+        flat[1:] = vv.reshape(-1)
+        vv = flat[1:].view(vv.shape)
+    tq.tq_encode_append(gpu, vv, bank, torch.from_numpy(pos.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    gb, gn, gr = download_bank(bank)
+    W = gb.shape[2]
+    report = {}
+    for b in range(banks):
+        slots = np.arange(pos[b], pos[b] + count)
+        words = gb[b].transpose(0, 2, 1).reshape(-1, W)[slots]
+        ref = oracle.encode_trace(orc, vals[b])
+        ref_rows = ref[0].transpose(0, 2, 1).reshape(-1, W)
+        pad = (-count) % 16
+        tiles = np.concatenate([words, ref_rows[count:]]).reshape(-1, 16, W).transpose(0, 2, 1)
+        check_encode((tiles, np.concatenate([gn[b][slots], np.zeros((pad, 1), np.float32)]),
+                      np.concatenate([gr[b][slots], np.zeros(pad, np.float32)])), ref, orc, count, report)
+        untouched = np.setdiff1d(np.arange(bank.n_pad), slots)
+        assert (gb[b].transpose(0, 2, 1).reshape(-1, W)[untouched] == 0x5A5A5A5A).all()
+        assert (gn[b][untouched] == -1.0).all() and (gr[b][untouched] == -2.0).all()
+    say("report", report)

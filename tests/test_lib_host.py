@@ -213,7 +213,7 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert good.workspace_bytes(tq.TQ_OP_ATTEND, 2, 0, 4) == 0
     def att(kp=good, keys=kb, vp=vals, values=vb, banks=2, n=100, q=0x1000, G=4, scale=0.125, out=0x8000,
             ws=0x100000, ws_bytes=need):
-        return At(kp.ref, keys, vp.ref, values, banks, n, q, G, scale, out, ws, ws_bytes, None)
+        return At(kp.ref, keys, vp.ref, values, banks, n, None, q, G, scale, out, ws, ws_bytes, None)
     assert att(kp=vals) == tq.TQ_ERR_UNSUPPORTED
     assert att(vp=patched(m=16)) == tq.TQ_ERR_ARG
     assert att(vp=_with_fake_ptrs(tq, d=256, m=0, groups=((256, 2),))) == tq.TQ_ERR_UNSUPPORTED
