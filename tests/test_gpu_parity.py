@@ -308,8 +308,10 @@ def test_encode_full_decode8b_layer_sampled(tq):
 
 def test_longctx_full_size_sampled(tq):
     """Long-context workload at full size (8 banks x 131072 bf16 keys, two channel groups
-    at 2 and 1 codebook bits, one 128-row sketch): GPU encoding on 2048 sampled keys and
-    GPU scores on sampled pairs, both against the oracle."""
+    at 2 and 1 codebook bits, one 128-row sketch): GPU encoding on 2048 sampled keys against
+    the oracle's encoding of them, and GPU scores at full size on random bank bytes (every
+    byte pattern with positive norms is a valid scorer input) on sampled pairs against the
+    oracle's estimates for the same bytes."""
     import torch
 
     cfg = workloads.CONFIGS["longctx"]
@@ -332,12 +334,16 @@ def test_longctx_full_size_sampled(tq):
     check_encode((gathered, bank.norms[bt, kt].cpu().numpy(), bank.rnorms[bt, kt].cpu().numpy()),
                  oracle.encode_trace(orc, sk), orc, 2048, rep)
     say("report", rep)
-    gb = download_bank(bank)
+    del bank, scores
+    W, npad, _ = gpu.layout(cfg.tokens)
+    rb, rn, rr = workloads.random_bank(cfg.cfg_id, cfg.banks, npad, W, 2)
+    rbank = upload_bank(tq, gpu, rb, rn, rr, cfg.tokens)
+    scores = tq.tq_score(gpu, rbank, q).cpu().numpy()
     qh = q.cpu().numpy()
     for b in g.choice(cfg.banks, 4, replace=False):
         kk = np.concatenate([g.integers(0, cfg.tokens, 400), [0, cfg.tokens - 1]])
         qi = g.integers(0, cfg.G, len(kk))
-        ref = oracle.score_pairs(orc, gb[0][b], gb[1][b], gb[2][b], qh[b], qi, kk)
+        ref = oracle.score_pairs(orc, rb[b], rn[b], rr[b], qh[b], qi, kk)
         check_scores(scores[b, qi, kk], ref, f"bank {b}")
 
 
