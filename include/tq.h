@@ -143,7 +143,9 @@ size_t tq_workspace_bytes(int op, const tq_params *p, int64_t banks, int64_t n, 
 
 /* Encode (stages 1 and 2) keys (device) [banks][n][d] of dtype TQ_F32 or TQ_BF16
  * into `out` (device arrays sized by tq_bank_layout for `banks` banks). Uses
- * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, ...). */
+ * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, ...). An MSE-only layout
+ * (m = 0: stage 1 alone, e.g. stored values) is supported up to d = 128
+ * (TQ_ERR_UNSUPPORTED above). */
 int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t n, const tq_bank *out,
               void *workspace, size_t ws_bytes, void *stream);
 
@@ -157,7 +159,8 @@ int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, in
  * tq_encode encodes them (up to the decision band of the fp32-level contractions). Uses
  * `workspace` (device) of tq_workspace_bytes(TQ_OP_ENCODE, p, banks, count, ...) bytes;
  * flags: 0 or TQ_APPEND_PREPARED (any other bit: TQ_ERR_ARG). Scoring a bank filled this way
- * uses n = n_cap: slots never written hold whatever the arrays held. TQ_ERR_UNSUPPORTED when
+ * uses n = n_cap: slots never written hold whatever the arrays held (tq_attend's lengths
+ * restrict attention to each bank's filled prefix). TQ_ERR_UNSUPPORTED when
  * the per-tile LDS footprint (16 keys x (8 d + 2 (d + m)) bytes) exceeds 150 KiB. */
 int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
                      const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
