@@ -25,6 +25,9 @@
  *   - Results are bit-identical from run to run for identical inputs.
  *   - Calls are thread-safe; the library holds no mutable global state.
  *   - Non-finite inputs give unspecified (but memory-safe) results.
+ *   - The matrices (rot, proj) and the bank arrays read by the scorers, top-k, decode and
+ *     attention are read with 16-byte loads: their pointers must be 16-byte aligned
+ *     (TQ_ERR_ARG otherwise). Allocations from hipMalloc or torch are.
  *
  * Packed bank format (one "bank" = the keys of one (layer, batch, kv-head), or a
  * whole search database). With W = sum_g b_g*d_g/32 + m/32 words per key and

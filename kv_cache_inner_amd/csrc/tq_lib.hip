@@ -223,6 +223,13 @@ extern "C" int tq_make_rotation(int d, const float *gauss, float *rot) {
 // ----------------------------------------------------------------------------------------
 // argument checks and geometry
 // ----------------------------------------------------------------------------------------
+static inline bool misaligned16(const void *ptr) { return ((uintptr_t)ptr & 15) != 0; }
+
+// The scorers, top-k and attention read bank arrays with 16-byte loads.
+static inline bool bank_misaligned(const tq_bank *b) {
+    return misaligned16(b->bits) || misaligned16(b->norms) || misaligned16(b->rnorms);
+}
+
 static int check_params(const tq_params *p) {
     if (!p) return TQ_ERR_ARG;
     if (p->n_groups < 1 || p->n_groups > 2) return TQ_ERR_ARG;
@@ -245,6 +252,7 @@ static int check_params(const tq_params *p) {
     // m = 0: codes and norms only (the MSE-only quantiser, e.g. for stored values)
     if (p->m != 0 && (p->m < 32 || p->m > 1024 || p->m % 32)) return TQ_ERR_ARG;
     if (!p->rot || (p->m > 0 && !p->proj)) return TQ_ERR_ARG;
+    if (misaligned16(p->rot) || misaligned16(p->proj)) return TQ_ERR_ARG;  // read as 16-byte rows
     return TQ_OK;
 }
 
@@ -768,7 +776,7 @@ extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t 
     if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
-    if (!in || !in->bits || !in->norms || !in->rnorms || !scores) return TQ_ERR_ARG;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !scores || bank_misaligned(in)) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     const ScoreScale sc = score_scale(p);
     return with_layout(p, [&](auto l) {
@@ -796,7 +804,7 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
     if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
-    if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q) return TQ_ERR_ARG;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q || bank_misaligned(in)) return TQ_ERR_ARG;
     hipStream_t st = (hipStream_t)stream;
     rc = G > 16 ? (int)TQ_ERR_UNSUPPORTED : with_layout(p, [&](auto l) {
         using L = decltype(l);
@@ -825,7 +833,7 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
     if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1 || k < 1 || k > 64 || k > n) return TQ_ERR_ARG;
     if (banks == 0) return TQ_OK;
-    if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx) return TQ_ERR_ARG;
+    if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx || bank_misaligned(in)) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     if (ws_bytes < tq_workspace_bytes(TQ_OP_TOPK, p, banks, n, G, k)) return TQ_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -881,6 +889,7 @@ extern "C" int tq_decode(const tq_params *p, const tq_bank *in, int64_t banks, i
     if (banks < 0 || n < 0) return TQ_ERR_ARG;
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !out) return TQ_ERR_ARG;
+    if (misaligned16(in->bits) || misaligned16(in->norms)) return TQ_ERR_ARG;
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     const DecArgs a = dec_args(p);
@@ -942,6 +951,7 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
     if (!keys || !keys->bits || !keys->norms || !keys->rnorms || !values || !values->bits || !values->norms || !q ||
         !out)
         return TQ_ERR_ARG;
+    if (bank_misaligned(keys) || misaligned16(values->bits) || misaligned16(values->norms)) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     const size_t need = tq_workspace_bytes(TQ_OP_ATTEND, kp, banks, n, G, 0);
     if (!need) return TQ_ERR_UNSUPPORTED;

@@ -225,6 +225,16 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert att(ws_bytes=need - 256) == tq.TQ_ERR_WORKSPACE
     assert att(banks=0, keys=ctypes.byref(nullbank), values=ctypes.byref(nullbank), q=None, out=None, ws=None,
                ws_bytes=0) == tq.TQ_OK
+    # 16-byte alignment of the matrices and of the banks the scorers read
+    odd = _with_fake_ptrs(tq)
+    odd.struct.rot = 0x10004
+    assert L.tq_bank_layout(odd.ref, 10, None, None, None) == tq.TQ_ERR_ARG
+    oddbank = tq.tq_bank(0x30000, 0x40008, 0x50000)
+    assert L.tq_score(good.ref, ctypes.byref(oddbank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 1 << 20,
+                      None) == tq.TQ_ERR_ARG
+    assert L.tq_topk(good.ref, ctypes.byref(oddbank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4000, 1 << 20,
+                     None) == tq.TQ_ERR_ARG
+    assert att(keys=ctypes.byref(oddbank)) == tq.TQ_ERR_ARG
     # empty inputs are valid no-ops
     assert L.tq_encode(good.ref, None, 0, 0, 10, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
     assert L.tq_encode(good.ref, None, 0, 3, 0, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
