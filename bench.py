@@ -211,7 +211,22 @@ def cpu_baseline(cfg, bits, banks, layers):
             oracle.score(orc, *encs[b], n, q[b])
         t_score += time.perf_counter() - t0
     pairs = banks * n * cfg.G * layers
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.set_threads(0)
+    # one core, on one bank and one layer's queries
+    prev = oracle.set_threads(1)
+    q = workloads.queries(cfg, 0, banks=[0])
+    t0 = time.perf_counter()
+    oracle.score(orc, *encs[0], n, q[0])
+    t_one = time.perf_counter() - t0
+    oracle.set_threads(prev)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": pairs / t_score,
         "unit": "pairs/s",
@@ -221,6 +236,9 @@ def cpu_baseline(cfg, bits, banks, layers):
                   f"G={cfg.G} queries of each of {layers} layers ({pairs} pairs, score {t_score:.1f}s); "
                   f"oracle encode of those keys {t_enc:.1f}s ({banks * n / t_enc:.3g} keys/s)",
         "encode_keys_per_s": banks * n / t_enc,
+        "cpu_model": cpu_model,
+        "one_core": {"value": n * cfg.G / t_one, "unit": "pairs/s",
+                     "sample": f"1 bank x {n} keys x G={cfg.G} queries, {t_one:.2f}s"},
     }
 
 
@@ -442,6 +460,45 @@ def attend_extra(tq, device, layers=4, reps=12):
     }
 
 
+def small_extra(tq, device, reps=20):
+    """The small workloads, whose banks stay in the last-level cache, so a call is bound by
+    launch latency rather than HBM: microseconds per tq_encode and per tq_score call for
+    tiny (1 x 1024 fp32 keys, G=16, b=3) and decode3b (2 x 8192 bf16 keys, G=8, b=3 and 4)."""
+    import torch
+    import workloads
+
+    out = {}
+    for name, bits in (("tiny", 3), ("decode3b", 3), ("decode3b", 4)):
+        cfg = workloads.CONFIGS[name]
+        prm = params_for(tq, cfg, bits, device)
+        keys = torch.from_numpy(workloads.keys(cfg)).to(device)
+        if cfg.key_dtype == "bf16":
+            keys = keys.to(torch.bfloat16)
+        q = torch.from_numpy(workloads.queries(cfg)).to(device)
+        bank = tq.Bank(prm, cfg.banks, cfg.tokens, device)
+        ews = torch.empty(max(prm.workspace_bytes(tq.TQ_OP_ENCODE, cfg.banks, cfg.tokens), 256), dtype=torch.uint8,
+                          device=device)
+        sws = tq.score_workspace(prm, bank, cfg.G)
+        scores = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        res = {}
+        for label, fn in (("encode_us", lambda: tq.tq_encode(prm, keys, bank, workspace=ews)),
+                          ("score_us", lambda: tq.tq_score(prm, bank, q, scores=scores, workspace=sws))):
+            for _ in range(3):
+                fn()
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            res[label] = a.elapsed_time(b) / reps * 1e3
+        res["pairs"] = cfg.banks * cfg.tokens * cfg.G
+        res["keys"] = cfg.banks * cfg.tokens
+        out[f"{name}_b{bits}"] = res
+    out["note"] = "cache-resident banks: per-call latency, not an HBM rate"
+    return out
+
+
 def search_extra(tq, device):
     """Vector search: 2,000,000 x 768 unit vectors, 1024 queries, top-10 per query, at
     b=4 and b=2; encode rate, top-k rate and recall@10 against the exact inner products."""
@@ -500,6 +557,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (calibrates the HBM traffic counters)")
+    ap.add_argument("--only", choices=["attend", "longctx", "search", "append", "variants", "small"],
+                    help="run one extra section alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build measures one GPU only: every bank is independent, so more "
@@ -514,6 +573,11 @@ def main():
 
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only:
+        fn = {"attend": attend_extra, "longctx": longctx_extra, "search": search_extra, "append": append_extra,
+              "variants": variants_extra, "small": small_extra}[args.only]
+        print(json.dumps({args.only: fn(tq, device)}))
+        return
     cfg = workloads.CONFIGS["decode8b"]
     L = args.layers
     if args.copy_mib:
@@ -560,6 +624,9 @@ def main():
             "layers": L, "banks_per_layer": cfg.banks, "keys_per_bank": cfg.tokens, "G": cfg.G, "d": cfg.d,
             "bits": 3, "bytes_per_key": sw3.bytes_per_key,
         },
+        "step_ms_percentiles": {"p10": float(np.percentile(kern_ms, 10)) * L,
+                                "median": float(np.median(kern_ms)) * L,
+                                "p90": float(np.percentile(kern_ms, 90)) * L},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "roofline": {
@@ -625,6 +692,8 @@ def main():
         log("streaming append")
         out["append"] = append_extra(tq, device)
         torch.cuda.empty_cache()
+        log("small workloads (latency)")
+        out["small"] = small_extra(tq, device)
         log("decode attention")
         out["attend"] = attend_extra(tq, device)
         torch.cuda.empty_cache()

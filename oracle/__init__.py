@@ -45,6 +45,11 @@ def lib():
     return _lib
 
 
+def set_threads(n: int) -> int:
+    """Threads of the oracle's OpenMP loops from now on; returns the previous count."""
+    return int(lib().orc_set_threads(int(n)))
+
+
 def _p(a: np.ndarray, ct=ctypes.c_void_p):
     return a.ctypes.data_as(ct)
 

@@ -44,6 +44,9 @@
  *   norms[key][g] (float32), rnorms[key] (float32).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -76,6 +79,19 @@ static int cfg_check(const orc_cfg *c) {
 }
 
 int orc_words_per_key(const orc_cfg *c) { return cfg_check(c) ? ORC_EARG : cfg_words(c); }
+
+/* Threads of the OpenMP loops from here on (the benchmark times the oracle on one core
+ * too); returns the previous count, or 1 without OpenMP. */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    if (n > 0) omp_set_num_threads(n);
+    return prev;
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------------ */
 /* Lloyd-Max codebook for the standard normal (stage 1's "precomputed codebook").   */
