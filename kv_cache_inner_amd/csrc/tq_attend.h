@@ -43,17 +43,8 @@ struct AttnArgs {
     double inv_sqrt_d[2];
 };
 
-__device__ __forceinline__ float at_wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ double at_wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+__device__ __forceinline__ float at_wave_max(float v) { return dpp_wave_max_f32(v); }
+__device__ __forceinline__ double at_wave_sum(double v) { return dpp_wave_sum_f64(v); }
 
 // 4 x 4 byte transpose: out[b] byte k = in[k] byte b.
 __device__ __forceinline__ u32x4 at_transpose_bytes(u32x4 x) {

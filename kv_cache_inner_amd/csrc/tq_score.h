@@ -248,9 +248,7 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
             }
         }
 #pragma unroll
-        for (int o = 1; o < CPR; o <<= 1)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) acc[qq] += __shfl_xor(acc[qq], o, 64);
+        for (int qq = 0; qq < 4; ++qq) acc[qq] = group_sum_f32<CPR>(acc[qq]);  // the CPR parts of a row
         // row-block partials: max |w| and the fp64 sum of the fp32 values
         float mx[4];
         double sm[4];
@@ -261,12 +259,10 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
             sm[qq] = part == 0 ? (double)acc[qq] : 0.0;
         }
 #pragma unroll
-        for (int o = CPR; o < 64; o <<= 1)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                mx[qq] = fmaxf(mx[qq], __shfl_xor(mx[qq], o, 64));
-                sm[qq] += __shfl_xor(sm[qq], o, 64);
-            }
+        for (int qq = 0; qq < 4; ++qq) {  // the rows of the wave (lanes congruent modulo CPR)
+            mx[qq] = stride_max_f32<CPR>(mx[qq]);
+            sm[qq] = stride_sum_f64<CPR>(sm[qq]);
+        }
         if (lane == 0)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
