@@ -57,8 +57,6 @@ struct PrepScratch {
     using PD = PrepDims<L, RT>;
     float qsrc[2][L::D][4 * RT];         // [0]: queries column-major; [1]: columns in group order
     float w[4 * RT][PD::NR];             // R_g q_g (group order) then S q
-    float pmax[PD::NR / PD::RB][4 * RT];   // per row-block max |w|
-    double psum[PD::NR / PD::RB][4 * RT];  // per row-block sum of w
     int F[4 * RT][L::NCLS];
 };
 
@@ -69,14 +67,12 @@ struct PrepView {
     using PD = PrepDims<L, RT>;
     float (&qsrc)[2][L::D][4 * RT];
     float (&w)[4 * RT][PD::NR];
-    float (&pmax)[PD::NR / PD::RB][4 * RT];
-    double (&psum)[PD::NR / PD::RB][4 * RT];
     int (&F)[4 * RT][L::NCLS];
 };
 
 template <class L, int RT>
 __device__ __forceinline__ PrepView<L, RT> view_of(PrepScratch<L, RT> &s) {
-    return PrepView<L, RT>{s.qsrc, s.w, s.pmax, s.psum, s.F};
+    return PrepView<L, RT>{s.qsrc, s.w, s.F};
 }
 
 // One GEMV item of the query preparation: (row tile, matrix row, part). Part p of a row
@@ -195,10 +191,9 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
     using PS = PrepDims<L, RT>;
     using PI = PrepItem<L, RT>;
     constexpr int NQ4 = 4 * RT;
-    constexpr int NR = PS::NR, CPR = PS::CPR, RB = PS::RB;
+    constexpr int NR = PS::NR, CPR = PS::CPR;
     constexpr int CH = PI::CH;
     static_assert(CH % 4 == 0 && 64 % CPR == 0, "bad chunking");
-    static_assert(L::D0 % RB == 0 && L::D % RB == 0, "row blocks must not straddle estimator terms");
     const int lane = tid & 63, wv = tid / 64;
     for (int e = tid; e < NQ4 * L::D; e += NT) {
         const int qq = e / L::D, c = e % L::D, gq = q0 + qq;
@@ -249,39 +244,29 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
         }
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) acc[qq] = group_sum_f32<CPR>(acc[qq]);  // the CPR parts of a row
-        // row-block partials: max |w| and the fp64 sum of the fp32 values
-        float mx[4];
-        double sm[4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
+        for (int qq = 0; qq < 4; ++qq)
             if (part == 0) ps.w[qb + qq][r] = acc[qq];
-            mx[qq] = fabsf(acc[qq]);
-            sm[qq] = part == 0 ? (double)acc[qq] : 0.0;
-        }
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {  // the rows of the wave (lanes congruent modulo CPR)
-            mx[qq] = stride_max_f32<CPR>(mx[qq]);
-            sm[qq] = stride_sum_f64<CPR>(sm[qq]);
-        }
-        if (lane == 0)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                ps.pmax[r / RB][qb + qq] = mx[qq];
-                ps.psum[r / RB][qb + qq] = sm[qq];
-            }
     }
     prep_barrier<LDS_ONLY>();
     hook(2);
-    // per (query, term): exponent F from the max |weight|, additive constant from the sum
-    for (int it = tid; it < NQ4 * L::NCLS; it += NT) {
+    // per (query, term): exponent F from the max |weight|, additive constant from the fp64 sum
+    // of the fp32 weights; one wave per (query, term), its lanes over the term's rows, reduced
+    // on the vector ALU
+    for (int it = wv; it < NQ4 * L::NCLS; it += NT / 64) {
         const int qq = it / L::NCLS, c = it % L::NCLS, gq = q0 + qq;
         const int r0 = c < L::NG ? (c ? L::D0 : 0) : L::D;
         const int r1 = c < L::NG ? (c ? L::D : L::D0) : NR;
-        double mx = 0.0, sm = 0.0;
-        for (int bk = r0 / RB; bk < r1 / RB; ++bk) {
-            mx = fmax(mx, (double)ps.pmax[bk][qq]);
-            sm += ps.psum[bk][qq];
+        float mxf = 0.0f;
+        double sm = 0.0;
+        for (int rr = r0 + lane; rr < r1; rr += 64) {
+            const float w = ps.w[qq][rr];
+            mxf = fmaxf(mxf, fabsf(w));
+            sm += (double)w;
         }
+        const double mx = (double)dpp_wave_max_f32(mxf);
+        sm = dpp_wave_sum_f64(sm);
+        if (lane == 0) {
         // (kernel-argument arrays are indexed with constants only: a runtime index would
         // read them through vector memory)
         double wmax;
@@ -301,6 +286,7 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
         ps.F[qq][c] = F;
         out.cst(qq, c, 0) = ldexp(1.0, -F);
         out.cst(qq, c, 1) = gq < G ? (c < L::NG ? -(c ? pa.cmax[1] : pa.cmax[0]) * sm : -sm) : 0.0;
+        }
     }
     prep_barrier<LDS_ONLY>();
     hook(3);
@@ -741,8 +727,6 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     // the first ones then never wait for direct-to-LDS loads into the ring
     __shared__ float s_qsrc[2][L::D][4];
     __shared__ float s_w[4][PD::NR];
-    __shared__ float s_pmax[PD::NR / PD::RB][4];
-    __shared__ double s_psum[PD::NR / PD::RB][4];
     __shared__ int s_F[4][L::NCLS];
     __shared__ __attribute__((aligned(16))) uint32_t s_frags[L::NF][64][4];
     __shared__ double s_consts[4][L::NCLS][2];
@@ -787,7 +771,7 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
             }
     };
     fill_piece(0);
-    PrepView<L, 1> view{s_qsrc, s_w, s_pmax, s_psum, s_F};
+    PrepView<L, 1> view{s_qsrc, s_w, s_F};
     prep_finish<L, 1, RING_WAVES * 64, true>(pr, tid, q, bank, G, 0, rot, proj, chan, pa, view,
                                              OperandLds<L>{s_frags, s_consts}, fill_piece);
     lds_barrier();
