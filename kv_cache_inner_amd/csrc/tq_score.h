@@ -132,14 +132,16 @@ __device__ __forceinline__ void prep_load(PrepRegs<L, RT, NT> &pr, int tid, cons
                                           const float *__restrict__ proj, const int *__restrict__ chan) {
     using PR = PrepRegs<L, RT, NT>;
     constexpr int NQ4 = 4 * RT;
-    pr.qv = pr.qg = 0.0f;
-    if (tid < NQ4 * L::D) {
-        const int qq = tid / L::D, c = tid % L::D, gq = q0 + qq;
-        const float *qrow = q + ((size_t)bank * G + gq) * L::D;
-        if (gq < G) {
-            pr.qv = qrow[c];
-            pr.qg = chan ? qrow[chan[c]] : pr.qv;
-        }
+    {
+        // an unconditional load at a clamped address (a load inside a branch would be waited
+        // for where the branch joins, before the matrix loads below are even issued); the
+        // channel-permuted copy needs the channel list first and is read in prep_finish
+        const int e = min(tid, NQ4 * L::D - 1);
+        const int qq = e / L::D, c = e % L::D;
+        const float v = q[((size_t)bank * G + min(q0 + qq, G - 1)) * L::D + c];
+        const bool use = (NT <= NQ4 * L::D || tid < NQ4 * L::D) && q0 + qq < G;
+        pr.qv = __uint_as_float(__float_as_uint(v) & (use ? ~0u : 0u));  // a mask, not a branch
+        pr.qg = pr.qv;
     }
 #pragma unroll
     for (int k = 0; k < PR::PRE; ++k)
@@ -197,11 +199,13 @@ __device__ __forceinline__ void prep_finish(const PrepRegs<L, RT, NT> &pr, int t
     const int lane = tid & 63, wv = tid / 64;
     for (int e = tid; e < NQ4 * L::D; e += NT) {
         const int qq = e / L::D, c = e % L::D, gq = q0 + qq;
+        const float *qrow = q + ((size_t)bank * G + gq) * L::D;
         float a = pr.qv, b = pr.qg;
         if (e != tid) {
-            const float *qrow = q + ((size_t)bank * G + gq) * L::D;
             a = gq < G ? qrow[c] : 0.0f;
             b = gq < G ? qrow[chan ? chan[c] : c] : 0.0f;
+        } else if (chan) {
+            b = gq < G ? qrow[chan[c]] : 0.0f;
         }
         ps.qsrc[0][c][qq] = a;
         ps.qsrc[1][c][qq] = b;
