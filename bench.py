@@ -86,23 +86,23 @@ def groups_of(cfg, bits):
     return [(cfg.d, bits - 1)] if cfg.groups is None else [(dg, b - 1) for dg, b in cfg.groups]
 
 
-def params_for(tq, cfg, bits, device):
+def params_for(tq, cfg, bits, device, norm16=False):
     import workloads
 
     groups = groups_of(cfg, bits)
     gauss = workloads.rotation_gaussians(cfg.cfg_id, [g[0] for g in groups])
     S = workloads.projection(cfg.cfg_id, cfg.m, cfg.d)
-    return tq.make_params(cfg.d, cfg.m, groups, gauss, S, workloads.group_channels(cfg), device)
+    return tq.make_params(cfg.d, cfg.m, groups, gauss, S, workloads.group_channels(cfg), device, norm16=norm16)
 
 
 class Sweep:
     """Packed banks of all layers for one bit budget, plus per-layer queries."""
 
-    def __init__(self, tq, cfg, bits, layers, device, time_encode=False):
+    def __init__(self, tq, cfg, bits, layers, device, time_encode=False, norm16=False):
         import torch
 
         self.cfg, self.bits, self.layers = cfg, bits, layers
-        self.params = params_for(tq, cfg, bits, device)
+        self.params = params_for(tq, cfg, bits, device, norm16)
         self.banks, self.queries = [], []
         W, npad, bpk = self.params.layout(cfg.tokens)
         self.bytes_per_key = bpk
@@ -352,6 +352,31 @@ def append_extra(tq, device):
     return out
 
 
+def halfnorm_extra(tq, device, layers, steps, ref_launch_ms):
+    """The headline sweep with the 16-bit norm format: the same decode8b layers (b=3) encoded
+    with binary16 norms (4 bytes fewer per key) and scored by the same ring kernel."""
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    sw = Sweep(tq, cfg, 3, layers, device, norm16=True)
+    wall, kern = timed(lambda: sw.step(tq), steps, 2, layers)
+    nbytes = cfg.banks * cfg.tokens * (sw.bytes_per_key + 4 * cfg.G)
+    kavg = float(np.mean(kern))
+    gbps = nbytes / (kavg * 1e-3) / 1e9
+    out = {
+        "workload": "decode8b sweep as the headline, binary16 norms",
+        "value": cfg.banks * cfg.tokens * cfg.G * layers / (wall / steps),
+        "unit": "pairs/s",
+        "bytes_per_key": sw.bytes_per_key,
+        "avg_launch_ms": kavg,
+        "kernel_gbps": gbps,
+        "kernel_frac": gbps / HBM_PEAK_GBPS,
+        "launch_speedup_vs_f32_norms": ref_launch_ms / kavg,
+    }
+    del sw
+    return out
+
+
 def variants_extra(tq, device):
     """One decode8b layer (b=3) encoded and scored with the randomised Walsh-Hadamard rotation
     and the exact sphere-marginal codebook (same kernels, other parameters)."""
@@ -557,13 +582,12 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (calibrates the HBM traffic counters)")
-    ap.add_argument("--only", choices=["attend", "longctx", "search", "append", "variants", "small"],
+    ap.add_argument("--only", choices=["attend", "longctx", "search", "append", "variants", "small", "halfnorm"],
                     help="run one extra section alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU only: every bank is independent, so more "
-                                   "GPUs would each run this same single-GPU sweep on their own banks; "
-                                   "run with --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: every bank is independent, so more GPUs would each run "
+                                   "this same single-GPU sweep on their own banks; run with --gpus 1"}))
         sys.exit(2)
 
     import torch
@@ -575,7 +599,8 @@ def main():
     torch.cuda.set_device(0)
     if args.only:
         fn = {"attend": attend_extra, "longctx": longctx_extra, "search": search_extra, "append": append_extra,
-              "variants": variants_extra, "small": small_extra}[args.only]
+              "variants": variants_extra, "small": small_extra,
+              "halfnorm": lambda t, d: halfnorm_extra(t, d, args.layers, args.steps, float("nan"))}[args.only]
         print(json.dumps({args.only: fn(tq, device)}))
         return
     cfg = workloads.CONFIGS["decode8b"]
@@ -660,6 +685,9 @@ def main():
             "kernel_frac": b4_bytes / (np.mean(kern4) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         }
         del sw4
+        torch.cuda.empty_cache()
+        log("binary16 norms")
+        out["half_norms"] = halfnorm_extra(tq, device, L, max(args.steps // 2, 1), kavg)
         torch.cuda.empty_cache()
 
         log("fp32 unquantized-keys comparator")

@@ -37,8 +37,12 @@
  *          codebook bit-plane p < b_g, d_g/32 words (word k, bit t = bit p of the
  *          bucket index of rotated coordinate 32k+t of group g); then m/32 sign
  *          words (word k, bit t = [row 32k+t of S times the residual >= 0]).
- *   norms  (float)  [banks][n_pad][n_groups]: |x_g| per group.
- *   rnorms (float)  [banks][n_pad]: |residual| (0 for the MSE-only quantiser, m = 0).
+ *   norms  [banks][n_pad][n_groups]: |x_g| per group.
+ *   rnorms [banks][n_pad]: |residual| (0 for the MSE-only quantiser, m = 0).
+ *   Both norm arrays hold float32 values, or with tq_params.norm_dtype == TQ_F16 the
+ *   IEEE binary16 roundings of those float32 values (2 bytes each: the format variant
+ *   with 16-bit norms; the stage-1 residual is then taken against the reconstruction
+ *   from the rounded norm, so the sketch corrects the rounding too).
  *   Slots n..n_pad-1 hold the encoding of the zero vector.
  */
 #ifndef TQ_H
@@ -54,12 +58,12 @@ extern "C" {
 typedef enum {
     TQ_OK = 0,
     TQ_ERR_ARG = -1,         /* null pointer, bad size, inconsistent parameters */
-    TQ_ERR_UNSUPPORTED = -2, /* a valid request this build has no kernel for */
+    TQ_ERR_UNSUPPORTED = -2, /* a valid request the library has no kernel for */
     TQ_ERR_DEVICE = -3,      /* a HIP launch failed */
     TQ_ERR_WORKSPACE = -4    /* workspace missing or smaller than tq_workspace_bytes() */
 } tq_status;
 
-typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 typedef enum { TQ_OP_ENCODE = 0, TQ_OP_SCORE = 1, TQ_OP_TOPK = 2, TQ_OP_ATTEND = 3 } tq_op;
 
@@ -88,7 +92,14 @@ enum { TQ_APPEND_PREPARED = 1 };
  *   rot          (device) float32: group 0's d_0 x d_0 rotation row-major, then
  *                group 1's; rotated coordinate j of group g = row j . x_g
  *   proj         (device) float32 [m][d] row-major: S, columns in channel order (NULL
- *                when m == 0) */
+ *                when m == 0)
+ *   norm_dtype   storage of the bank's norm arrays: TQ_F32 (0), or TQ_F16 for the
+ *                16-bit norm format variant (turboquant-pytorch write-up, results: the
+ *                compressed cache size it reports at 3 bits is met with 16-bit norms).
+ *                TQ_F16 requires d <= 128 and m <= 128 (TQ_ERR_UNSUPPORTED otherwise,
+ *                from every entry point); tq_encode and tq_encode_append then need
+ *                16-byte aligned bits (tq_encode) and keys 16-byte (f32) or 8-byte
+ *                (bf16) aligned, else TQ_ERR_UNSUPPORTED. Other values: TQ_ERR_ARG. */
 typedef struct {
     int32_t d, m, n_groups;
     int32_t group_dim[2];
@@ -98,13 +109,14 @@ typedef struct {
     const int32_t *group_chan;
     const float *rot;
     const float *proj;
+    int32_t norm_dtype;
 } tq_params;
 
 /* (device) arrays of one or more banks, laid out as described above. */
 typedef struct {
     uint32_t *bits;
-    float *norms;
-    float *rnorms;
+    void *norms;  /* float32, or binary16 (tq_params.norm_dtype) */
+    void *rnorms;
 } tq_bank;
 
 /* Lloyd-Max codebook for N(0,1) with 2^bits levels, 1 <= bits <= 4, computed on
@@ -136,7 +148,7 @@ int tq_make_rotation_hadamard(int d, const float *signs, float *rot);
 int tq_make_rotation(int d, const float *gauss, float *rot);
 
 /* Bank geometry for n keys: 32-bit words per key, n_pad, and bytes per key of the
- * three arrays together (words*4 + 4*n_groups + 4). Host only. */
+ * three arrays together (words*4 + (n_groups + 1)*4, or *2 with 16-bit norms). Host only. */
 int tq_bank_layout(const tq_params *p, int64_t n, int64_t *words_per_key, int64_t *n_pad, int64_t *bytes_per_key);
 
 /* Device workspace bytes needed by `op` (a tq_op) for these sizes; 0 on bad

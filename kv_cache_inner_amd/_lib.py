@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtq.so")
 
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_DEVICE, TQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
-TQ_F32, TQ_BF16 = 0, 1
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_OP_ENCODE, TQ_OP_SCORE, TQ_OP_TOPK, TQ_OP_ATTEND = 0, 1, 2, 3
 TQ_APPEND_PREPARED = 1
 
@@ -34,6 +34,7 @@ class tq_params(ctypes.Structure):
         ("group_dim", ctypes.c_int32 * 2), ("group_bits", ctypes.c_int32 * 2),
         ("centroids", (ctypes.c_float * 16) * 2), ("thresholds", (ctypes.c_float * 15) * 2),
         ("group_chan", ctypes.c_void_p), ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
+        ("norm_dtype", ctypes.c_int32),
     ]
 
 
@@ -150,8 +151,9 @@ class Params:
     """tq_params plus the device tensors it points to (kept alive here)."""
 
     def __init__(self, d: int, m: int, groups: Sequence[Tuple[int, int]], rot, proj, chan=None,
-                 codebooks: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None):
+                 codebooks: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None, norm16: bool = False):
         self.d, self.m = d, m
+        self.norm16 = bool(norm16)
         self.groups = [(int(a), int(b)) for a, b in groups]
         self.rot, self.proj, self.chan = rot, proj, chan
         s = tq_params()
@@ -167,6 +169,7 @@ class Params:
                 s.thresholds[g][i] = float(v)
         s.group_chan = _ptr(chan)
         s.rot, s.proj = _ptr(rot), _ptr(proj)
+        s.norm_dtype = TQ_F16 if self.norm16 else TQ_F32
         self.struct = s
 
     @property
@@ -189,17 +192,17 @@ class Params:
 
 def make_params(d: int, m: int, groups: Sequence[Tuple[int, int]], gaussians: Sequence[np.ndarray], proj: np.ndarray,
                 chan: Optional[np.ndarray] = None, device="cuda", rotations: Optional[Sequence[np.ndarray]] = None,
-                codebooks: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None) -> Params:
+                codebooks: Optional[List[Tuple[np.ndarray, np.ndarray]]] = None, norm16: bool = False) -> Params:
     """Host construction of R (tq_make_rotation per group, unless explicit `rotations` are
     given) and the codebooks (tq_make_codebook unless `codebooks` are given), uploaded with
-    S and the channel list."""
+    S and the channel list. norm16: banks of these parameters store binary16 norms."""
     import torch
 
     rots = list(rotations) if rotations is not None else [tq_make_rotation(g) for g in gaussians]
     rot = torch.from_numpy(np.concatenate([r.ravel() for r in rots])).to(device)
     pj = None if proj is None else torch.from_numpy(np.ascontiguousarray(proj, dtype=np.float32)).to(device)
     ch = None if chan is None else torch.from_numpy(np.ascontiguousarray(chan, dtype=np.int32)).to(device)
-    return Params(d, m, groups, rot, pj, ch, codebooks=codebooks)
+    return Params(d, m, groups, rot, pj, ch, codebooks=codebooks, norm16=norm16)
 
 
 class Bank:
@@ -211,8 +214,9 @@ class Bank:
         W, npad, _ = params.layout(n)
         self.banks, self.n, self.n_pad, self.W = banks, n, npad, W
         self.bits = torch.zeros((banks, npad // 16, W, 16), dtype=torch.int32, device=device)
-        self.norms = torch.zeros((banks, npad, params.ng), dtype=torch.float32, device=device)
-        self.rnorms = torch.zeros((banks, npad), dtype=torch.float32, device=device)
+        nt = torch.float16 if params.norm16 else torch.float32
+        self.norms = torch.zeros((banks, npad, params.ng), dtype=nt, device=device)
+        self.rnorms = torch.zeros((banks, npad), dtype=nt, device=device)
         self.struct = tq_bank(self.bits.data_ptr(), self.norms.data_ptr(), self.rnorms.data_ptr())
 
     @property

@@ -76,9 +76,10 @@ constexpr int AT_WAIT_VM0 = (7 << 4) | (15 << 8);
 // word's stored planes for all tiles of the chunk, then the logits and norms of its
 // query; one wait covers them all, so a work-group costs one memory round trip and the
 // products run from LDS.
-template <int NG>
+// NH: the value bank stores binary16 norms.
+template <int NG, bool NH>
 __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
-    const float *__restrict__ scores, const uint32_t *__restrict__ vbits, const float *__restrict__ vnorms, long n,
+    const float *__restrict__ scores, const uint32_t *__restrict__ vbits, const void *__restrict__ vnorms, long n,
     int n_tiles, int G, int chunks, float scale, const int32_t *__restrict__ lengths, AttnArgs a,
     float *__restrict__ part) {
     constexpr int TILES = AT_CHUNK / 16;
@@ -132,15 +133,27 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
         const long len = lengths ? min((long)max(lengths[bank], 0), n) : n;
         const int nkv = (int)max(min((long)AT_CHUNK, len - k0), 0L);
         const float *sb = scores + ((size_t)bank * G + (qlive ? qg : 0)) * n + k0;
-        const float *nb = vnorms + ((size_t)bank * n_pad + k0) * NG;
+        const size_t nbase = ((size_t)bank * n_pad + k0) * NG;
         // loads at clamped addresses, all issued before the first wait (no branch around a
         // load: each would wait on its own)
         f32x4 nv[AT_RPL][NG];  // norms of keys 4 lane .. 4 lane + 3 (groups interleaved per key)
+        u32x4 nraw[AT_RPL];    // the same as binary16 pairs (4 NG halves), widened after the wait
 #pragma unroll
         for (int r = 0; r < AT_RPL; ++r) {
             const int kb = min(256 * r + 4 * lane, nkp - 4);
+            if constexpr (NH) {
+                const uint16_t *nb = static_cast<const uint16_t *>(vnorms) + nbase;
+                if constexpr (NG == 1) {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(nb + kb);
+                    nraw[r] = u32x4{v.x, v.y, 0u, 0u};
+                } else {
+                    nraw[r] = *reinterpret_cast<const u32x4 *>(nb + kb * NG);
+                }
+            } else {
+                const float *nb = static_cast<const float *>(vnorms) + nbase;
 #pragma unroll
-            for (int h = 0; h < NG; ++h) nv[r][h] = reinterpret_cast<const f32x4 *>(nb + kb * NG)[h];
+                for (int h = 0; h < NG; ++h) nv[r][h] = reinterpret_cast<const f32x4 *>(nb + kb * NG)[h];
+            }
         }
         float e[AT_RPL][4];
 #pragma unroll
@@ -148,6 +161,17 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
 #pragma unroll
             for (int k = 0; k < 4; ++k) e[r][k] = sb[min(256 * r + 4 * lane + k, nk - 1)];
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NH) {
+            // half e of a lane's block is norm (key e / NG, group e % NG), as float e above
+#pragma unroll
+            for (int r = 0; r < AT_RPL; ++r)
+#pragma unroll
+                for (int h = 0; h < NG; ++h) {
+                    const uint32_t w0 = nraw[r][2 * h], w1 = nraw[r][2 * h + 1];
+                    nv[r][h] = f32x4{norm_f32((uint16_t)w0), norm_f32((uint16_t)(w0 >> 16)),
+                                     norm_f32((uint16_t)w1), norm_f32((uint16_t)(w1 >> 16))};
+                }
+        }
         const float c2 = scale * 1.4426950408889634f;
         float mx = -INFINITY;
         if (nkv == AT_CHUNK) {
@@ -378,9 +402,10 @@ struct DecArgs {
     int gdim[2], goff[2], gbits[2], gword[2];
     float cent[2][8];
     float inv_sqrt_d[2];
+    int nh;  // 1: binary16 norms
 };
 
-__global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict__ bits, const float *__restrict__ norms,
+__global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict__ bits, const void *__restrict__ norms,
                                                      long n, int n_tiles, const float *__restrict__ rot,
                                                      const int *__restrict__ chan, DecArgs a, float *__restrict__ out) {
     extern __shared__ float s_c[];  // [16][d]
@@ -395,7 +420,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
         int idx = 0;
         for (int p = 0; p < a.gbits[g]; ++p)
             idx |= (int)((tw[(size_t)(a.gword[g] + p * (a.gdim[g] >> 5) + (jj >> 5)) * 16 + i] >> (jj & 31)) & 1u) << p;
-        const float nu = norms[((size_t)bank * n_pad + 16 * t + i) * a.ng + g];
+        const size_t ni = ((size_t)bank * n_pad + 16 * t + i) * a.ng + g;
+        const float nu = a.nh ? norm_f32(static_cast<const uint16_t *>(norms)[ni]) : static_cast<const float *>(norms)[ni];
         s_c[i * a.d + j] = a.cent[g][idx] * (nu * a.inv_sqrt_d[g]);
     }
     __syncthreads();

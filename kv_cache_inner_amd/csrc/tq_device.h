@@ -10,6 +10,7 @@ namespace tq {
 typedef int8_t i8x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Compile-time loop: calls f(std::integral_constant<int, I>) for I = 0..N-1.
@@ -23,6 +24,12 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Stored norms: float32, or the bits of an IEEE binary16 value (the 16-bit norm format;
+// v_cvt_f16_f32 rounds to nearest even, the widening back is exact).
+__device__ __forceinline__ float norm_f32(float v) { return v; }
+__device__ __forceinline__ float norm_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_binary16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 // Work-group barrier over LDS traffic only: it waits for this wave's LDS operations but not
 // for its vector-memory loads, so loads issued earlier (direct-to-LDS or into registers)

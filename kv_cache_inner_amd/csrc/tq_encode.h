@@ -33,6 +33,7 @@ struct EncArgs {
     float cent[2][16];
     float thr[2][15];
     double sqrt_d[2];
+    int nh;  // 1: the bank stores binary16 norms (encode_split_kernel only)
 };
 
 // S'[i][pos] for pos = goff[g] + j: sum_k S[i][chan[goff[g]+k]] * R_g[j][k] (fp64 sums in
@@ -497,7 +498,7 @@ template <typename KT>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
-    float *__restrict__ norms, float *__restrict__ rnorms, EncSlots slots) {
+    void *__restrict__ norms, void *__restrict__ rnorms, EncSlots slots) {
     constexpr int XP = sizeof(KT) == 2 ? 1 : 3;  // key pieces: bf16 keys are exact in one
     constexpr int PS = 4 * 64;                     // piece stride of the operand buffers (u32x4)
     __shared__ __align__(16) u32x4 XB[2][XP][4][64];
@@ -657,9 +658,18 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
                 inv = s > 0.0f ? (cq ? sqrt_d1 : sqrt_d0) / nu : 0.0f;
             }
             s_inv[buf][ik][cq] = inv;
-            s_coef[buf][ik][cq] = nu * (cq ? inv_sqrt_d1 : inv_sqrt_d0);
+            // the reconstruction (and so the residual) takes the stored norm: with binary16
+            // norms its rounding, which the sketch then corrects too
+            const uint16_t nu_h = f32_to_binary16(nu);
+            const float nu_st = a.nh ? norm_f32(nu_h) : nu;
+            s_coef[buf][ik][cq] = nu_st * (cq ? inv_sqrt_d1 : inv_sqrt_d0);
             const long fs = out_slot(T, ik);
-            if (fs >= 0) norms[(size_t)fs * ng + cq] = nu;
+            if (fs >= 0) {
+                if (a.nh)
+                    static_cast<uint16_t *>(norms)[(size_t)fs * ng + cq] = nu_h;
+                else
+                    static_cast<float *>(norms)[(size_t)fs * ng + cq] = nu;
+            }
         }
     };
 
@@ -738,7 +748,13 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
 #pragma unroll
                     for (int w = 0; w < ENCS_ROT; ++w) s += (double)s_rho[buf ^ 1][w][lane];
                     const long fs = out_slot(tp, lane);
-                    if (fs >= 0) rnorms[fs] = M > 0 ? (float)sqrt(s) : 0.0f;  // none stored for m = 0
+                    const float rv = M > 0 ? (float)sqrt(s) : 0.0f;  // none stored for m = 0
+                    if (fs >= 0) {
+                        if (a.nh)
+                            static_cast<uint16_t *>(rnorms)[fs] = f32_to_binary16(rv);
+                        else
+                            static_cast<float *>(rnorms)[fs] = rv;
+                    }
                 }
                 // project tile tp's residual, add its sign words
                 if (prj_live) {

@@ -42,6 +42,9 @@ struct Layout {
     static constexpr int D1 = NG_ > 1 ? D1_ : 0, B1 = NG_ > 1 ? B1_ : 0;
     static constexpr int M = M_;
     static constexpr int D = D0 + D1;
+    // the bank's norms: float32 here, binary16 in HalfNorms<Layout>
+    static constexpr bool NH = false;
+    using NormT = float;
     static constexpr int NCLS = NG + 1;
     static constexpr int SWG0 = B0 * D0 / 32, SWG1 = B1 * D1 / 32, SWS = M / 32;
     static constexpr int W = SWG0 + SWG1 + SWS;  // stored words per key
@@ -164,6 +167,13 @@ struct Layout {
     static constexpr int frag_q(int f) { return frag_field(f, 0); }
     static constexpr int frag_h(int f) { return frag_field(f, 1); }
     static constexpr int frag_c(int f) { return frag_field(f, 2); }
+};
+
+// The same layout with its bank's norms stored as binary16 (the 16-bit norm format).
+template <class L>
+struct HalfNorms : L {
+    static constexpr bool NH = true;
+    using NormT = uint16_t;
 };
 
 }  // namespace tq

@@ -253,8 +253,13 @@ static int check_params(const tq_params *p) {
     if (p->m != 0 && (p->m < 32 || p->m > 1024 || p->m % 32)) return TQ_ERR_ARG;
     if (!p->rot || (p->m > 0 && !p->proj)) return TQ_ERR_ARG;
     if (misaligned16(p->rot) || misaligned16(p->proj)) return TQ_ERR_ARG;  // read as 16-byte rows
+    if (p->norm_dtype != TQ_F32 && p->norm_dtype != TQ_F16) return TQ_ERR_ARG;
+    // binary16 norms: written by the d, m <= 128 encoder, read by the kernels of those layouts
+    if (p->norm_dtype == TQ_F16 && (p->d > 128 || p->m > 128)) return TQ_ERR_UNSUPPORTED;
     return TQ_OK;
 }
+
+static bool half_norms(const tq_params *p) { return p->norm_dtype == TQ_F16; }
 
 static int words_per_key(const tq_params *p) {
     int w = p->m / 32;
@@ -271,7 +276,7 @@ extern "C" int tq_bank_layout(const tq_params *p, int64_t n, int64_t *wpk, int64
     const int W = words_per_key(p);
     if (wpk) *wpk = W;
     if (n_pad) *n_pad = 16 * ((n + 15) / 16);
-    if (bpk) *bpk = 4 * (int64_t)W + 4 * (int64_t)p->n_groups + 4;
+    if (bpk) *bpk = 4 * (int64_t)W + (half_norms(p) ? 2 : 4) * ((int64_t)p->n_groups + 1);
     return TQ_OK;
 }
 
@@ -306,6 +311,22 @@ static int with_layout(const tq_params *p, F &&f) {
     TQ_LAYOUTS(TQ_TRY)
 #undef TQ_TRY
     return TQ_ERR_UNSUPPORTED;
+}
+
+// As with_layout, for the kernels that read a bank's norms: the layout as stored, wrapped
+// in HalfNorms for the 16-bit norm format (which the encoder writes for d, m <= 128 only).
+template <class F>
+static int with_bank_layout(const tq_params *p, F &&f) {
+    const bool h = half_norms(p);
+    return with_layout(p, [&](auto l) -> int {
+        using L = decltype(l);
+        if constexpr (L::D <= ENCS_DMAX && L::M <= ENCS_DMAX) {
+            if (h) return f(HalfNorms<L>{});
+            return f(l);
+        } else {
+            return h ? (int)TQ_ERR_UNSUPPORTED : (int)f(l);
+        }
+    });
 }
 
 // query-operand workspace: frags [banks][Gpad/4][NF][64][16 B], consts [banks][Gpad][NCLS][2] f64
@@ -451,6 +472,7 @@ static EncArgs enc_args(const tq_params *p) {
     }
     a.sword = word;
     a.W = word + p->m / 32;
+    a.nh = half_norms(p) ? 1 : 0;
     return a;
 }
 
@@ -473,15 +495,18 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (p->m == 0 && enc_large(p)) return TQ_ERR_UNSUPPORTED;  // MSE-only keys up to 128 dimensions
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+    // d, m <= 128 with aligned words: the persistent bf16-split encoder (the only one that
+    // writes binary16 norms)
+    const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)out->bits % 16) == 0 &&
+                       ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
+    if (half_norms(p) && !split) return TQ_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     const EncArgs a = enc_args(p);
     float *sp = (float *)workspace;
     const long tot = (long)p->m * p->d;
     launch_prep_proj(p, a, sp, st);
     if ((rc = launch_status())) return rc;
-    // d, m <= 128 with aligned words: the persistent bf16-split encoder
-    if (p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)out->bits % 16) == 0 &&
-        ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0) {
+    if (split) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         const int64_t total = banks * n_tiles;
@@ -519,18 +544,18 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
                 if (dtype == TQ_F32)
                     hipLaunchKernelGGL(enc_gemm_rot_kernel<float>, grid, dim3(EG_THREADS), 0, st, (const float *)keys,
                                        p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles, (long)n, jbase,
-                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, out->norms);
+                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, (float *)out->norms);
                 else
                     hipLaunchKernelGGL(enc_gemm_rot_kernel<uint16_t>, grid, dim3(EG_THREADS), 0, st,
                                        (const uint16_t *)keys, p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles,
                                        (long)n, jbase, (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits,
-                                       out->norms);
+                                       (float *)out->norms);
                 jbase += 2 * ntile;
             }
             const dim3 pgrid((unsigned)(kblocks * ((p->m + EG_TILE - 1) / EG_TILE)));
             hipLaunchKernelGGL(enc_gemm_prj_kernel, pgrid, dim3(EG_THREADS), 0, st, (const float *)(ws + ew.U),
                                (const uint16_t *)(ws + ew.s3), a, (long)tc, rows, ew.J, (const float *)(ws + ew.rho),
-                               out->bits, out->rnorms);
+                               out->bits, (float *)out->rnorms);
             if ((rc = launch_status())) return rc;
         }
         return TQ_OK;
@@ -541,12 +566,13 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (dtype == TQ_F32) {
         (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)n, (int)n_tiles,
-                           p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, EncSlots{nullptr, 0});
+                           p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms, (float *)out->rnorms,
+                           EncSlots{nullptr, 0});
     } else {
         (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)n,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms,
-                           EncSlots{nullptr, 0});
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
+                           (float *)out->rnorms, EncSlots{nullptr, 0});
     }
     return launch_status();
 }
@@ -566,6 +592,8 @@ extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype,
     if (banks * n_tiles > INT32_MAX || cap_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     const size_t smem = enc_smem_bytes(p->d, p->m);
     if (smem > 150 * 1024) return TQ_ERR_UNSUPPORTED;
+    const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
+    if (half_norms(p) && !split) return TQ_ERR_UNSUPPORTED;  // binary16 norms: the split encoder only
     hipStream_t st = (hipStream_t)stream;
     const EncArgs a = enc_args(p);
     float *sp = (float *)workspace;
@@ -574,7 +602,7 @@ extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype,
         if ((rc = launch_status())) return rc;
     }
     const EncSlots slots{pos, (int)cap_tiles};
-    if (p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0) {
+    if (split) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         const int64_t total = banks * n_tiles;
@@ -593,11 +621,13 @@ extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype,
     if (dtype == TQ_F32) {
         (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)count,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
+                           (float *)out->rnorms, slots);
     } else {
         (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)count,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
+                           (float *)out->rnorms, slots);
     }
     return launch_status();
 }
@@ -683,7 +713,7 @@ static int launch_score(const tq_bank *in, int64_t banks, int64_t n, int32_t G, 
     const int8_t *frags = (const int8_t *)ws;
     const double *consts = (const double *)((const char *)ws + pl.const_off);
     hipLaunchKernelGGL((score_kernel<L, RT, score_tb<L, RT>()>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
-                       in->bits, in->norms, in->rnorms, frags, consts, scores, (int)banks, (long)n, (int)n_tiles, (int)G,
+                       in->bits, (const typename L::NormT *)in->norms, (const typename L::NormT *)in->rnorms, frags, consts, scores, (int)banks, (long)n, (int)n_tiles, (int)G,
                        pl.Gpad, (int)tpw, (int)wpb, sc);
     return launch_status();
     }
@@ -714,7 +744,7 @@ static int launch_fused(const tq_params *p, const tq_bank *in, int64_t banks, in
         wpb = (n_tiles + tpw - 1) / tpw;
         if (banks * wpb > INT32_MAX) return TQ_ERR_UNSUPPORTED;
         hipLaunchKernelGGL((score_fused_kernel<L, RT, score_tb<L, RT>()>), dim3((unsigned)(banks * wpb)),
-                           dim3(WAVES * 64), 0, st, in->bits, in->norms, in->rnorms, q, p->rot, p->proj,
+                           dim3(WAVES * 64), 0, st, in->bits, (const typename L::NormT *)in->norms, (const typename L::NormT *)in->rnorms, q, p->rot, p->proj,
                            p->group_chan, prep_args(p), scores, (int)banks, (long)n, (int)n_tiles, (int)G, (int)wpb,
                            (int)tpw, score_scale(p));
         return launch_status();
@@ -743,7 +773,7 @@ static int launch_ring(const tq_params *p, const tq_bank *in, int64_t banks, int
         wpb = (n_tiles + tpw - 1) / tpw;
         if (banks * wpb > INT32_MAX || 4 * n > INT32_MAX) return TQ_ERR_UNSUPPORTED;
         hipLaunchKernelGGL((score_ring_kernel<L, ring_slots<L>()>), dim3((unsigned)(banks * wpb)),
-                           dim3(RING_WAVES * 64), 0, st, in->bits, in->norms, in->rnorms, q, p->rot, p->proj,
+                           dim3(RING_WAVES * 64), 0, st, in->bits, (const typename L::NormT *)in->norms, (const typename L::NormT *)in->rnorms, q, p->rot, p->proj,
                            p->group_chan, prep_args(p), scores, (int)banks, (long)n, (int)n_tiles, (int)G, (int)wpb,
                            (int)tpw, score_scale(p));
         return launch_status();
@@ -763,7 +793,7 @@ static int launch_lds(const tq_bank *in, int64_t banks, int64_t n, int32_t G, co
         const int8_t *frags = (const int8_t *)ws;
         const double *consts = (const double *)((const char *)ws + pp.const_off);
         hipLaunchKernelGGL((score_lds_kernel<L, lds_rows<L>(), TOPK>), dim3((unsigned)lp.grid), dim3(LDS_WAVES * 64),
-                           0, st, in->bits, in->norms, in->rnorms, frags, consts, (long)n, (int)((n + 15) / 16), (int)G,
+                           0, st, in->bits, (const typename L::NormT *)in->norms, (const typename L::NormT *)in->rnorms, frags, consts, (long)n, (int)((n + 15) / 16), (int)G,
                            pp.Gpad, lp.qblocks, lp.kchunks, lp.chunk_tiles, sc, scores, (int)k, part_v, part_i);
         return launch_status();
     }
@@ -779,7 +809,7 @@ extern "C" int tq_score_prepared(const tq_params *p, const tq_bank *in, int64_t 
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores || bank_misaligned(in)) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     const ScoreScale sc = score_scale(p);
-    return with_layout(p, [&](auto l) {
+    return with_bank_layout(p, [&](auto l) {
         using L = decltype(l);
         const PrepPlan pl = prep_plan(L::NF, L::NCLS, banks, G);
         hipStream_t st = (hipStream_t)stream;
@@ -806,7 +836,7 @@ extern "C" int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, in
     if (banks == 0 || n == 0) return TQ_OK;
     if (!in || !in->bits || !in->norms || !in->rnorms || !scores || !q || bank_misaligned(in)) return TQ_ERR_ARG;
     hipStream_t st = (hipStream_t)stream;
-    rc = G > 16 ? (int)TQ_ERR_UNSUPPORTED : with_layout(p, [&](auto l) {
+    rc = G > 16 ? (int)TQ_ERR_UNSUPPORTED : with_bank_layout(p, [&](auto l) {
         using L = decltype(l);
         switch ((G + 3) / 4) {
             case 1: {
@@ -838,7 +868,7 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
     if (ws_bytes < tq_workspace_bytes(TQ_OP_TOPK, p, banks, n, G, k)) return TQ_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     const ScoreScale sc = score_scale(p);
-    return with_layout(p, [&](auto l) {
+    return with_bank_layout(p, [&](auto l) {
         using L = decltype(l);
         if constexpr (!lds_fits<L>()) {
             return (int)TQ_ERR_UNSUPPORTED;
@@ -880,6 +910,7 @@ static DecArgs dec_args(const tq_params *p) {
         for (int i = 0; i < (1 << p->group_bits[g]); ++i) a.cent[g][i] = p->centroids[g][i];
         a.inv_sqrt_d[g] = (float)(1.0 / sqrt((double)p->group_dim[g]));
     }
+    a.nh = half_norms(p) ? 1 : 0;
     return a;
 }
 
@@ -968,12 +999,14 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
     hipStream_t st = (hipStream_t)stream;
     const int64_t n_tiles = (n + 15) / 16;
     const dim3 grid((unsigned)(banks * chunks), (unsigned)((G + 3) / 4));
+    auto chunk_kernel = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(AT_THREADS), 0, st, logits, values->bits, (const void *)values->norms,
+                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
+    };
     if (vp->n_groups == 1)
-        hipLaunchKernelGGL(attn_chunk_kernel<1>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
-                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
+        half_norms(vp) ? chunk_kernel(attn_chunk_kernel<1, true>) : chunk_kernel(attn_chunk_kernel<1, false>);
     else
-        hipLaunchKernelGGL(attn_chunk_kernel<2>, grid, dim3(AT_THREADS), 0, st, logits, values->bits, values->norms,
-                           (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
+        half_norms(vp) ? chunk_kernel(attn_chunk_kernel<2, true>) : chunk_kernel(attn_chunk_kernel<2, false>);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(64), 0, st, part, (int)chunks, vp->rot,
                        vp->group_chan, a, out);

@@ -438,8 +438,8 @@ struct TileBatch {
 template <class L, int RT, int TB>
 struct TileStream {
     const uint32_t *__restrict__ bb;  // this bank's tiles (wave-uniform)
-    const float *__restrict__ nb;     // its norms
-    const float *__restrict__ rb;     // its residual norms
+    const typename L::NormT *__restrict__ nb;  // its norms
+    const typename L::NormT *__restrict__ rb;  // its residual norms
     float *__restrict__ ob;           // its score rows
     long n;
     int G, t0, t1;  // wave-uniform
@@ -474,10 +474,10 @@ struct TileStream {
                 const uint32_t v = tb[woff[s]];
                 b.sw[t][s] = wlive[s] ? v : 0u;
             }
-            const float *tn = nb + (size_t)tile * (16 * L::NG);
+            const typename L::NormT *tn = nb + (size_t)tile * (16 * L::NG);
 #pragma unroll
-            for (int g = 0; g < L::NG; ++g) b.nu[t][g] = tn[j * L::NG + g];
-            b.rho[t] = rb[(size_t)tile * 16 + j];
+            for (int g = 0; g < L::NG; ++g) b.nu[t][g] = norm_f32(tn[j * L::NG + g]);
+            b.rho[t] = norm_f32(rb[(size_t)tile * 16 + j]);
         }
     }
 
@@ -537,8 +537,10 @@ struct TileStream {
 
 // Scorer on prepared operands (tq_score_prepared): operands read from the workspace.
 template <class L, int RT, int TB>
-__global__ __launch_bounds__(256) void score_kernel(const uint32_t *__restrict__ bits, const float *__restrict__ norms,
-                                                    const float *__restrict__ rnorms, const int8_t *__restrict__ frags,
+__global__ __launch_bounds__(256) void score_kernel(const uint32_t *__restrict__ bits,
+                                                    const typename L::NormT *__restrict__ norms,
+                                                    const typename L::NormT *__restrict__ rnorms,
+                                                    const int8_t *__restrict__ frags,
                                                     const double *__restrict__ consts, float *__restrict__ scores,
                                                     int banks, long n, int n_tiles, int G, int Gpad, int tiles_per_wave,
                                                     int waves_per_bank, ScoreScale sc) {
@@ -594,10 +596,10 @@ struct FusedLds {
 
 template <class L, int RT, int TB>
 __global__ __launch_bounds__(fused_waves<RT>() * 64) void score_fused_kernel(
-    const uint32_t *__restrict__ bits, const float *__restrict__ norms, const float *__restrict__ rnorms,
-    const float *__restrict__ q, const float *__restrict__ rot, const float *__restrict__ proj,
-    const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks, long n, int n_tiles, int G,
-    int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
+    const uint32_t *__restrict__ bits, const typename L::NormT *__restrict__ norms,
+    const typename L::NormT *__restrict__ rnorms, const float *__restrict__ q, const float *__restrict__ rot,
+    const float *__restrict__ proj, const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks,
+    long n, int n_tiles, int G, int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
     __shared__ FusedLds<L, RT> lds;
     const long bank = blockIdx.x / wgs_per_bank;
     const int part = blockIdx.x % wgs_per_bank;
@@ -677,11 +679,20 @@ constexpr int ring_slots() {
     return (s > 8 ? 8 : s) & ~1;  // even: the steady state fills the ring by halves
 }
 
+// Norms per 16-byte lane load (4 float32 or 8 binary16), and the lanes that load a tile's
+// norm rows (the group norms, then the residual norms).
+template <class L>
+struct NormRows {
+    static constexpr int PER = 16 / (int)sizeof(typename L::NormT);
+    static constexpr int NU_LANES = 16 * L::NG / PER;
+    static constexpr int LANES = NU_LANES + 16 / PER;
+};
+
 // Issues the direct loads of one tile into a slot (every lane of the wave calls it):
 // `tile_bits` is the tile's bit block, `nr_src` this lane's 16 bytes of the tile's norm
-// rows (lanes below 4*NG: norms; the next four lanes: residual norms; see NormLane).
+// rows (see NormLane).
 template <class L>
-__device__ __forceinline__ void ring_fetch(const char *tile_bits, const float *nr_src, lds_u32 *slot, int lane) {
+__device__ __forceinline__ void ring_fetch(const char *tile_bits, const void *nr_src, lds_u32 *slot, int lane) {
     static_for<RingTile<L>::BIT_LOADS>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         constexpr int rows = L::W - 16 * i < 16 ? L::W - 16 * i : 16;
@@ -689,20 +700,23 @@ __device__ __forceinline__ void ring_fetch(const char *tile_bits, const float *n
             __builtin_amdgcn_global_load_lds(tile_bits + 1024 * i + 16 * lane, (lds_void *)(slot + 256 * i), 16, 0,
                                              0);
     });
-    if (lane < 4 * (L::NG + 1)) __builtin_amdgcn_global_load_lds(nr_src, (lds_void *)(slot + 16 * L::W), 16, 0, 0);
+    if (lane < NormRows<L>::LANES)
+        __builtin_amdgcn_global_load_lds(nr_src, (lds_void *)(slot + 16 * L::W), 16, 0, 0);
 }
 
 // A lane's share of the norm rows: its source for tile 0 and its stride per tile.
 template <class L>
 struct NormLane {
-    const float *base;
-    int stride;  // floats per tile
-    __device__ __forceinline__ NormLane(const float *nb, const float *rb, int lane) {
-        const bool is_nu = lane < 4 * L::NG;
-        base = is_nu ? nb + 4 * lane : rb + 4 * (lane - 4 * L::NG);
+    using T = typename L::NormT;
+    const T *base;
+    int stride;  // norms per tile
+    __device__ __forceinline__ NormLane(const T *nb, const T *rb, int lane) {
+        using NR = NormRows<L>;
+        const bool is_nu = lane < NR::NU_LANES;
+        base = is_nu ? nb + NR::PER * lane : rb + NR::PER * (lane - NR::NU_LANES);
         stride = is_nu ? 16 * L::NG : 16;
     }
-    __device__ __forceinline__ const float *at(int tile) const { return base + (size_t)tile * stride; }
+    __device__ __forceinline__ const T *at(int tile) const { return base + (size_t)tile * stride; }
 };
 
 template <class L>
@@ -721,10 +735,10 @@ __device__ __forceinline__ void ring_wait(int ahead) {
 
 template <class L, int S>
 __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
-    const uint32_t *__restrict__ bits, const float *__restrict__ norms, const float *__restrict__ rnorms,
-    const float *__restrict__ q, const float *__restrict__ rot, const float *__restrict__ proj,
-    const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks, long n, int n_tiles, int G,
-    int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
+    const uint32_t *__restrict__ bits, const typename L::NormT *__restrict__ norms,
+    const typename L::NormT *__restrict__ rnorms, const float *__restrict__ q, const float *__restrict__ rot,
+    const float *__restrict__ proj, const int *__restrict__ chan, PrepArgs pa, float *__restrict__ scores, int banks,
+    long n, int n_tiles, int G, int wgs_per_bank, int tiles_per_wg, ScoreScale sc) {
     using RTL = RingTile<L>;
     using PD = PrepDims<L, 1>;
     // the preparation's scratch, operands and ring as separate LDS arrays: LDS accesses to
@@ -745,8 +759,8 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     const int nt = t1 - t0;
     const long n_pad = (long)n_tiles * 16;
     const uint32_t *bb = bits + (size_t)bank * n_tiles * L::W * 16;
-    const float *nb = norms + (size_t)bank * n_pad * L::NG;
-    const float *rb = rnorms + (size_t)bank * n_pad;
+    const typename L::NormT *nb = norms + (size_t)bank * n_pad * L::NG;
+    const typename L::NormT *rb = rnorms + (size_t)bank * n_pad;
     float *ob = scores + (size_t)bank * G * n;
     lds_u32 *ring = (lds_u32 *)&ring_mem[wv][0][0];
     const NormLane<L> nl(nb, rb, lane);
@@ -810,32 +824,56 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     // loads, so the only waits on those are the explicit ones above. Lane group gl takes
     // word 4s+gl of key j (words past the tile's W are read from the slot's later rows and
     // dropped); norms of key j; residual norm of key j.
+    // With binary16 norms the norm rows are half as long: key j's norms at 2 (NG j + g)
+    // bytes into them, its residual norm at 2 j bytes past the NG group rows' 32 NG bytes.
     static_assert(4 * L::NSQ <= RingTile<L>::ROWS && L::NSQ <= 4 && L::NG <= 2, "slot read layout");
-    const uint32_t lane_w = 4u * lane, lane_n = 4u * j * L::NG, lane_r = 4u * j;
+    constexpr uint32_t NB = sizeof(typename L::NormT);
+    const uint32_t lane_w = 4u * lane, lane_n = NB * j * L::NG, lane_r = NB * j;
     auto read_slot = [&](const lds_u32 *slot, uint32_t(&sw)[L::NSQ], float(&nu)[L::NG], float &rho) {
         const uint32_t base = (uint32_t)(uintptr_t)slot;
         uint32_t w[4], nn[2], r;
         constexpr int O1 = (L::NSQ > 1 ? 1 : 0) * 256, O2 = (L::NSQ > 2 ? 2 : 0) * 256,
-                      O3 = (L::NSQ > 3 ? 3 : 0) * 256, ON = 64 * L::W, ON1 = 64 * L::W + (L::NG > 1 ? 4 : 0),
-                      OR = 64 * (L::W + L::NG);
-        asm volatile(
-            "ds_read_b32 %0, %7\n"
-            "ds_read_b32 %1, %7 offset:%10\n"
-            "ds_read_b32 %2, %7 offset:%11\n"
-            "ds_read_b32 %3, %7 offset:%12\n"
-            "ds_read_b32 %4, %8 offset:%13\n"
-            "ds_read_b32 %5, %8 offset:%14\n"
-            "ds_read_b32 %6, %9 offset:%15\n"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(nn[0]), "=&v"(nn[1]), "=&v"(r)
-            : "v"(base + lane_w), "v"(base + lane_n), "v"(base + lane_r), "i"(O1), "i"(O2), "i"(O3), "i"(ON),
-              "i"(ON1), "i"(OR)
-            : "memory");
+                      O3 = (L::NSQ > 3 ? 3 : 0) * 256, ON = 64 * L::W, ON1 = 64 * L::W + (L::NG > 1 ? (int)NB : 0),
+                      OR = 64 * L::W + 16 * (int)NB * L::NG;
+        if constexpr (L::NH)
+            asm volatile(
+                "ds_read_b32 %0, %7\n"
+                "ds_read_b32 %1, %7 offset:%10\n"
+                "ds_read_b32 %2, %7 offset:%11\n"
+                "ds_read_b32 %3, %7 offset:%12\n"
+                "ds_read_u16 %4, %8 offset:%13\n"
+                "ds_read_u16 %5, %8 offset:%14\n"
+                "ds_read_u16 %6, %9 offset:%15\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(nn[0]), "=&v"(nn[1]), "=&v"(r)
+                : "v"(base + lane_w), "v"(base + lane_n), "v"(base + lane_r), "i"(O1), "i"(O2), "i"(O3), "i"(ON),
+                  "i"(ON1), "i"(OR)
+                : "memory");
+        else
+            asm volatile(
+                "ds_read_b32 %0, %7\n"
+                "ds_read_b32 %1, %7 offset:%10\n"
+                "ds_read_b32 %2, %7 offset:%11\n"
+                "ds_read_b32 %3, %7 offset:%12\n"
+                "ds_read_b32 %4, %8 offset:%13\n"
+                "ds_read_b32 %5, %8 offset:%14\n"
+                "ds_read_b32 %6, %9 offset:%15\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(nn[0]), "=&v"(nn[1]), "=&v"(r)
+                : "v"(base + lane_w), "v"(base + lane_n), "v"(base + lane_r), "i"(O1), "i"(O2), "i"(O3), "i"(ON),
+                  "i"(ON1), "i"(OR)
+                : "memory");
 #pragma unroll
         for (int s = 0; s < L::NSQ; ++s) sw[s] = wlive[s] ? w[s] : 0u;
+        if constexpr (L::NH) {
 #pragma unroll
-        for (int g = 0; g < L::NG; ++g) nu[g] = __uint_as_float(nn[g]);
-        rho = __uint_as_float(r);
+            for (int g = 0; g < L::NG; ++g) nu[g] = norm_f32((uint16_t)nn[g]);
+            rho = norm_f32((uint16_t)r);
+        } else {
+#pragma unroll
+            for (int g = 0; g < L::NG; ++g) nu[g] = __uint_as_float(nn[g]);
+            rho = __uint_as_float(r);
+        }
     };
     auto tile_est = [&](const uint32_t(&sw)[L::NSQ], const float(&nu)[L::NG], float rho) -> float {
         i32x4 acc[1][L::NCLS];

@@ -69,8 +69,8 @@ __device__ __forceinline__ void topk_offer(float &lv, int &li, float est, int ke
 
 template <class L, int RQ, bool TOPK>
 __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
-    const uint32_t *__restrict__ bits, const float *__restrict__ norms, const float *__restrict__ rnorms,
-    const int8_t *__restrict__ frags, const double *__restrict__ consts, long n, int n_tiles, int G, int Gpad,
+    const uint32_t *__restrict__ bits, const typename L::NormT *__restrict__ norms,
+    const typename L::NormT *__restrict__ rnorms, const int8_t *__restrict__ frags, const double *__restrict__ consts, long n, int n_tiles, int G, int Gpad,
     int qblocks, int kchunks, int chunk_tiles, ScoreScale sc, float *__restrict__ scores, int k,
     float *__restrict__ part_v, int *__restrict__ part_i) {
     __shared__ __attribute__((aligned(16))) int8_t fa[RQ][L::NF][64][16];

@@ -30,7 +30,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("m", ctypes.c_int), ("ng", ctypes.c_int),
                 ("gdim", ctypes.c_int * 2), ("gbits", ctypes.c_int * 2),
-                ("chan", ctypes.POINTER(ctypes.c_int))]
+                ("chan", ctypes.POINTER(ctypes.c_int)), ("norm16", ctypes.c_int)]
 
 
 _lib = None
@@ -57,10 +57,15 @@ def _p(a: np.ndarray, ct=ctypes.c_void_p):
 class Spec:
     """Shape of one encoding: dimension d, sign-sketch rows m (0 = MSE-only),
     channel groups [(d_g, b_g)] with b_g the codebook bits of group g, and the
-    channel list (group 0's channels then group 1's; None = identity)."""
+    channel list (group 0's channels then group 1's; None = identity). norm16: the
+    format variant whose norms are stored at binary16 precision (the binary16 rounding of
+    the float32 norm; the residual is taken against the reconstruction from that stored
+    norm)."""
 
-    def __init__(self, d: int, m: int, groups: Sequence[tuple], chan: Optional[np.ndarray] = None):
+    def __init__(self, d: int, m: int, groups: Sequence[tuple], chan: Optional[np.ndarray] = None,
+                 norm16: bool = False):
         self.d, self.m = d, m
+        self.norm16 = bool(norm16)
         self.groups = [(int(a), int(b)) for a, b in groups]
         self.chan = None if chan is None else np.ascontiguousarray(chan, dtype=np.int32)
         c = _Cfg()
@@ -68,6 +73,7 @@ class Spec:
         for g, (dg, bg) in enumerate(self.groups):
             c.gdim[g], c.gbits[g] = dg, bg
         c.chan = _p(self.chan, ctypes.POINTER(ctypes.c_int)) if self.chan is not None else None
+        c.norm16 = int(self.norm16)
         self._c = c
 
     @property
@@ -323,3 +329,11 @@ def bucketize(z: float, thresholds: np.ndarray) -> int:
     t = np.ascontiguousarray(thresholds, dtype=np.float32)
     lib().orc_bucketize.argtypes = [ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
     return lib().orc_bucketize(ctypes.c_float(z), _p(t), len(t) + 1)
+
+
+def round_binary16(x: float) -> float:
+    """The IEEE binary16 value nearest to the float32 x (ties to even), as a float."""
+    f = lib().orc_round_binary16
+    f.argtypes = [ctypes.c_float]
+    f.restype = ctypes.c_float
+    return float(f(ctypes.c_float(x)))

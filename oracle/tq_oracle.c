@@ -27,7 +27,10 @@
  *   - the codebook is Lloyd-Max for N(0,1) and is applied to the rotated
  *     coordinates scaled to unit variance, z = sqrt(d_g) * (R x)_j / |x|;
  *   - each vector (and each channel group) keeps its norm as float32, the
- *     residual keeps its norm rho as float32;
+ *     residual keeps its norm rho as float32; the format variant with 16-bit norms
+ *     stores the binary16 rounding of those float32 values, and the reconstruction
+ *     that the residual is taken against uses the stored (rounded) norm, so the
+ *     sketch corrects exactly what a reader of the bytes rebuilds;
  *   - the sign-sketch scale is sqrt(pi/2)/m * rho (Gaussian sign identity);
  *   - bucket index = number of thresholds t with z >= t (ties go up), with the
  *     decision taken on z rounded to float32 against float32 thresholds;
@@ -58,6 +61,7 @@ typedef struct {
     int d, m, ng;
     int gdim[2], gbits[2];
     const int *chan; /* [d]: group 0 channels then group 1 channels; NULL = identity */
+    int norm16;      /* 1: norms stored at IEEE binary16 precision (format variant) */
 } orc_cfg;
 
 static int cfg_chan(const orc_cfg *c, int pos) { return c->chan ? c->chan[pos] : pos; }
@@ -70,6 +74,7 @@ static int cfg_words(const orc_cfg *c) {
 
 static int cfg_check(const orc_cfg *c) {
     if (c->ng < 1 || c->ng > 2 || c->d <= 0 || c->d > 1024 || c->m < 0 || c->m > 1024 || c->m % 32) return ORC_EARG;
+    if (c->norm16 != 0 && c->norm16 != 1) return ORC_EARG;
     int s = 0;
     for (int g = 0; g < c->ng; ++g) {
         if (c->gdim[g] <= 0 || c->gdim[g] % 32 || c->gbits[g] < 1 || c->gbits[g] > 4) return ORC_EARG;
@@ -255,6 +260,30 @@ int orc_rotation(int d, const float *gauss, double *rot) {
     return ORC_OK;
 }
 
+/* The IEEE 754 binary16 value nearest to x (ties to even), returned as a float: 11
+ * significant bits for |x| >= 2^-14, a multiple of 2^-24 below that, infinity from
+ * 65520 (the midpoint above the largest finite value, 65504) up. Scaling by a power of
+ * two and rint (round-to-nearest-even, the default mode) are exact in double. */
+static float round_binary16(float x) {
+    if (x == 0.0f || isnan(x) || isinf(x)) return x;
+    const double a = fabs((double)x);
+    if (a >= 65520.0) return x > 0 ? INFINITY : -INFINITY;
+    int e;
+    (void)frexp(a, &e); /* a = f 2^e, f in [0.5, 1): leading bit 2^(e-1) */
+    const int lead = e - 1 < -14 ? -14 : e - 1;
+    const double quantum = ldexp(1.0, lead - 10);
+    const double r = rint(a / quantum) * quantum;
+    return (float)(x > 0 ? r : -r);
+}
+
+/* A stored norm: float32, or (format variant) the binary16 rounding of that float32. */
+static float stored_norm(const orc_cfg *c, double v) {
+    const float f = (float)v;
+    return c->norm16 ? round_binary16(f) : f;
+}
+
+float orc_round_binary16(float x) { return round_binary16(x); }
+
 /* ------------------------------------------------------------------------------ */
 /* Encode: stage 1 (rotate, quantise per coordinate) + stage 2 (residual signs).    */
 /* ------------------------------------------------------------------------------ */
@@ -307,7 +336,7 @@ int orc_encode_trace(const orc_cfg *c, const double *rot, const float *proj, con
                 nu2 += v * v;
             }
             const double nu = sqrt(nu2);
-            const float nu_s = (float)nu;
+            const float nu_s = stored_norm(c, nu);
             norms[key * c->ng + g] = nu_s;
             for (int j = 0; j < dg; ++j) {
                 double s = 0.0;
@@ -339,7 +368,7 @@ int orc_encode_trace(const orc_cfg *c, const double *rot, const float *proj, con
                 r[k] = x[k] - xhat[k];
                 rho2 += r[k] * r[k];
             }
-            rnorms[key] = (float)sqrt(rho2);
+            rnorms[key] = stored_norm(c, sqrt(rho2));
             for (int i = 0; i < m; ++i) {
                 double p = 0.0;
                 for (int k = 0; k < d; ++k) p += (double)proj[(long)i * d + k] * r[k];

@@ -312,6 +312,52 @@ def test_residual_signs_and_norms_are_those_of_the_decoder(seed):
     np.testing.assert_allclose(s0, ref, rtol=1e-11, atol=1e-11)
 
 
+def test_binary16_rounding_is_the_ieee_nearest_value():
+    # against numpy's float16 conversion (an independent implementation of IEEE 754
+    # round-to-nearest-even), over many binades, the subnormal range, ties and overflow
+    g = np.random.default_rng(77)
+    x = (g.standard_normal(20000) * 10.0 ** g.integers(-9, 5, 20000)).astype(np.float32)
+    edge = np.float32([0.0, 65504.0, 65519.0, 65520.0, 65536.0, 2.0 ** -14, 2.0 ** -24, 2.0 ** -25,
+                       1.5 * 2.0 ** -25, 1e-9, -3.5, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2049.0, 2051.0])
+    for v in np.concatenate([x, edge]):
+        with np.errstate(over="ignore"):
+            ref = float(np.float16(v))
+        assert oracle.round_binary16(float(v)) == ref, v
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_binary16_norm_variant_stores_rounded_norms_and_corrects_their_reconstruction(seed):
+    # the format variant: stored norms are the binary16 roundings of the float32 norms; the
+    # codes are those of the float32 format; the residual (its norm and its signs) is the one
+    # left by the reconstruction from the stored bytes
+    g = np.random.default_rng(300 + seed)
+    d = int(g.choice([64, 128]))
+    m = int(g.choice([32, 128]))
+    b = int(g.integers(1, 4))
+    G = g.standard_normal((d, d)).astype(np.float32)
+    S = g.standard_normal((m, d)).astype(np.float32)
+    x = (g.standard_normal((40, d)) * g.uniform(0.01, 50, (40, 1))).astype(np.float32)
+    spec32 = oracle.Spec(d, m, [(d, b)])
+    spec16 = oracle.Spec(d, m, [(d, b)], norm16=True)
+    b32, n32, _ = oracle.encode(oracle.Params(spec32, [G], S), x)
+    prm = oracle.Params(spec16, [G], S)
+    bits, norms, rnorms = oracle.encode(prm, x)
+    np.testing.assert_array_equal(norms, n32.astype(np.float16).astype(np.float32))
+    np.testing.assert_array_equal(norms[:40, 0],
+                                  np.linalg.norm(x.astype(np.float64), axis=1).astype(np.float32)
+                                  .astype(np.float16).astype(np.float32))
+    codes32, _ = oracle.unpack(spec32, b32, 40)
+    codes16, signs = oracle.unpack(spec16, bits, 40)
+    np.testing.assert_array_equal(codes16, codes32)
+    r = x.astype(np.float64) - oracle.decode(prm, bits, norms, 40)
+    rho16 = np.linalg.norm(r, axis=1).astype(np.float32).astype(np.float16).astype(np.float32)
+    assert np.abs(rnorms[:40] - rho16).max() <= 2.0 ** -10 * rho16.max()
+    assert (rnorms[:40] == rho16).mean() > 0.9
+    p = r @ S.astype(np.float64).T
+    clear = np.abs(p) > 1e-9 * np.abs(p).max()
+    np.testing.assert_array_equal(signs[clear], (p[clear] >= 0).astype(np.uint8))
+
+
 def test_zero_key_contributes_nothing():
     spec = oracle.Spec(128, 128, [(128, 3)])
     g = np.random.default_rng(9)
@@ -499,6 +545,26 @@ def test_estimator_unbiased_with_closed_form_variance_over_projections():
     var = ((math.pi / 2) * rho ** 2 * (qd @ qd) - (qd @ r) ** 2) / d
     rel = est.var(ddof=1) / var
     assert abs(rel - 1) < 4 * math.sqrt(2 / (len(est) - 1))
+
+
+@pytest.mark.slow
+def test_binary16_norm_variant_estimator_stays_unbiased():
+    # with the residual taken against the rounded-norm reconstruction the sketch corrects
+    # the rounding too: the estimate stays unbiased over projections
+    g = np.random.default_rng(37)
+    d = 128
+    x = (g.standard_normal(d) * 7).astype(np.float32)
+    q = (x / 3 + g.standard_normal(d)).astype(np.float32)
+    G = g.standard_normal((d, d)).astype(np.float32)
+    spec = oracle.Spec(d, d, [(d, 1)], norm16=True)
+    prm = oracle.Params(spec, [G], np.zeros((d, d), np.float32))
+    est = np.empty(3000)
+    for s in range(len(est)):
+        prm.proj = np.random.default_rng(7000 + s).standard_normal((d, d)).astype(np.float32)
+        b_, n_, r_ = oracle.encode(prm, x[None])
+        est[s] = oracle.score(prm, b_, n_, r_, 1, q[None])[0, 0]
+    truth = float(q.astype(np.float64) @ x.astype(np.float64))
+    assert abs(est.mean() - truth) < 4 * est.std(ddof=1) / math.sqrt(len(est))
 
 
 @pytest.mark.slow
