@@ -690,7 +690,8 @@ struct NormRows {
 
 // Issues the direct loads of one tile into a slot (every lane of the wave calls it):
 // `tile_bits` is the tile's bit block, `nr_src` this lane's 16 bytes of the tile's norm
-// rows (see NormLane).
+// rows (see NormLane). Every tile is read once, so the loads carry the non-temporal cache
+// hint (aux = 2, the nt bit; measured about 0.7 % faster than the default policy).
 template <class L>
 __device__ __forceinline__ void ring_fetch(const char *tile_bits, const void *nr_src, lds_u32 *slot, int lane) {
     static_for<RingTile<L>::BIT_LOADS>([&](auto ic) {
@@ -698,10 +699,10 @@ __device__ __forceinline__ void ring_fetch(const char *tile_bits, const void *nr
         constexpr int rows = L::W - 16 * i < 16 ? L::W - 16 * i : 16;
         if (rows == 16 || lane < 4 * rows)
             __builtin_amdgcn_global_load_lds(tile_bits + 1024 * i + 16 * lane, (lds_void *)(slot + 256 * i), 16, 0,
-                                             0);
+                                             2);
     });
     if (lane < NormRows<L>::LANES)
-        __builtin_amdgcn_global_load_lds(nr_src, (lds_void *)(slot + 16 * L::W), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(nr_src, (lds_void *)(slot + 16 * L::W), 16, 0, 2);
 }
 
 // A lane's share of the norm rows: its source for tile 0 and its stride per tile.
@@ -898,6 +899,31 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     int i = 0;
     const int full = (int)(n >> 4);  // tiles whose 16 keys are all below n
     const int loff = gl * (int)n + j;  // lane offset into the bank's score rows
+    // Scores of a group of four tiles leave as one 16-byte store per lane: a 4 x 4 transpose
+    // inside each lane quad (tile index <-> key bits 0-1) gives lane 4c + x the keys
+    // 4c .. 4c + 3 of tile x, so a query row's 16 lanes cover 256 contiguous bytes with one
+    // instruction. Rows must start 16-byte aligned (n a multiple of 4).
+    const bool wide = U == 4 && (n & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+    const int wide_off = gl * (int)n + 16 * (lane & 3) + 4 * ((lane >> 2) & 3);
+    auto store_group = [&](float *base, const float(&pv)[U]) {
+        if constexpr (U == 4) {
+            float v0 = pv[0], v1 = pv[1], v2 = pv[2], v3 = pv[3];
+            const bool o = lane & 1, h = lane & 2;
+            float r = dpp_mov_f32<DPP_XOR1>(o ? v0 : v1);
+            v0 = o ? r : v0;
+            v1 = o ? v1 : r;
+            r = dpp_mov_f32<DPP_XOR1>(o ? v2 : v3);
+            v2 = o ? r : v2;
+            v3 = o ? v3 : r;
+            r = dpp_mov_f32<DPP_XOR2>(h ? v0 : v2);
+            v0 = h ? r : v0;
+            v2 = h ? v2 : r;
+            r = dpp_mov_f32<DPP_XOR2>(h ? v1 : v3);
+            v1 = h ? r : v1;
+            v3 = h ? v3 : r;
+            *reinterpret_cast<f32x4 *>(base + wide_off) = f32x4{v0, v1, v2, v3};
+        }
+    };
     if (G == 4 && 2 * S <= nt && t0 + U <= full) {
         float pend[U];
         auto group = [&](auto store_prev) {
@@ -910,7 +936,13 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
                 uint32_t sw[L::NSQ];
                 float nu[L::NG], rho;
                 read_slot(half + k * RTL::WORDS, sw, nu, rho);
-                if constexpr (SP) prev_out[loff + 16 * k] = pend[k];
+                if constexpr (SP) {
+                    if (wide) {
+                        if (k == 0) store_group(prev_out, pend);
+                    } else {
+                        prev_out[loff + 16 * k] = pend[k];
+                    }
+                }
                 const int tn = t0 + i + S + k;
                 ring_fetch<L>(tile_bits<L>(bb, tn), nl.at(tn), half + k * RTL::WORDS, lane);
                 pend[k] = tile_est(sw, nu, rho);
@@ -920,10 +952,14 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
         group(std::false_type{});
         while (i + S + U <= nt && t0 + i + U <= full) group(std::true_type{});
         float *last_out = ob + (size_t)(t0 + i - U) * 16;
-        static_for<U>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            last_out[loff + 16 * k] = pend[k];
-        });
+        if (wide) {
+            store_group(last_out, pend);
+        } else {
+            static_for<U>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                last_out[loff + 16 * k] = pend[k];
+            });
+        }
     }
     // the rest one tile at a time: waits by the loads actually issued after the tile,
     // refills while inside the run, stores checked against G and n

@@ -141,6 +141,29 @@ def test_score_random_banks_full_decode8b_layer(tq):
             check_scores(got[b, qi, ki], ref, f"bank {b}")
 
 
+@pytest.mark.parametrize("offset", [0, 1])
+def test_score_ring_steady_state_every_output(tq, offset):
+    """256 banks x 4100 keys (one work-group per bank, 17 tiles on most waves: the ring's
+    steady state with its grouped stores, then a ragged last tile), G = 4, on random bank
+    bytes; every score against the oracle. offset = 1 places the score rows 4 bytes off a
+    16-byte boundary (the per-tile store path)."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    banks, n = 256, 4100
+    gpu, orc = both_params(cfg, 3)
+    W, npad, _ = gpu.layout(n)
+    rb, rn, rr = workloads.random_bank(cfg.cfg_id, banks, npad, W, 1, layer=5)
+    bank = upload_bank(tq, gpu, rb, rn, rr, n)
+    q = np.random.default_rng(11).standard_normal((banks, 4, cfg.d)).astype(np.float32)
+    flat = torch.full((banks * 4 * n + offset,), float("nan"), dtype=torch.float32, device="cuda")
+    scores = flat[offset:].view(banks, 4, n)
+    say(f"ring steady state: {banks} x {n}, score offset {offset}")
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda(), scores=scores).cpu().numpy()
+    for b in range(banks):
+        check_scores(got[b], oracle.score(orc, rb[b], rn[b], rr[b], n, q[b]), f"bank {b}")
+
+
 # ------------------------------------------------------------------------------------------
 # encoder against the oracle's encoding of the same keys
 # ------------------------------------------------------------------------------------------
