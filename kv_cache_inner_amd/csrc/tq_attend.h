@@ -117,7 +117,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
             const int rt = gb == 1 ? row : (gb == 2 ? row >> 1 : (row * 43691) >> 17);  // row / gb
             const int tile = min(t_first + rt, n_tiles - 1), p = row - rt * gb;
             __builtin_amdgcn_global_load_lds(vb + ((size_t)tile * a.W + wbase + p * pstride) * 16 + 4 * (lane & 3),
-                                             (at_lds_void *)&s_v[wv][16 * i][0], 16, 0, 0);
+                                             (at_lds_void *)&s_v[wv][16 * i][0], 16, 0,
+                                             2);  // nt: each value row is read once
         }
     }
 
