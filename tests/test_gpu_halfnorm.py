@@ -163,3 +163,28 @@ def test_half_norm_decode_and_attend(tq):
         tol = np.expm1(2 * scale * e) * A + 1e-6 * (A + np.sqrt((v ** 2).mean()))
         err = np.abs(out[b].astype(np.float64) - ref)
         assert (err <= tol).all(), f"bank {b}: worst excess {np.max(err - tol):.3e}"
+
+
+def test_half_norm_full_decode8b_layer_sampled(tq):
+    """The full 8B-class layer (64 banks x 32768 keys, G = 4) with binary16 norms, in the
+    benchmark's launch configuration, on random bank bytes (binary16 norms of random
+    positive values); sampled pairs against the oracle."""
+    import torch
+
+    cfg = workloads.CONFIGS["decode8b"]
+    gpu, orc = both_params(cfg, 3, norm16=True)
+    W, npad, bpk = gpu.layout(cfg.tokens)
+    assert bpk == 4 * W + 4
+    rb, rn, rr = workloads.random_bank(cfg.cfg_id, cfg.banks, npad, W, 1, layer=3)
+    rn = rn.astype(np.float16).astype(np.float32)  # values the format can hold
+    rr = rr.astype(np.float16).astype(np.float32)
+    bank = upload_bank(tq, gpu, rb, rn, rr, cfg.tokens)
+    q = workloads.queries(cfg, layer=3)
+    say("half-norm full layer, random bank")
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+    g = np.random.default_rng(16)
+    for b in g.choice(cfg.banks, 6, replace=False):
+        ki = np.concatenate([g.integers(0, cfg.tokens, 250), [0, cfg.tokens - 1]])
+        qi = g.integers(0, cfg.G, len(ki))
+        ref = oracle.score_pairs(orc, rb[b], rn[b], rr[b], q[b], qi, ki)
+        check_scores(got[b, qi, ki], ref, f"bank {b}")
