@@ -317,28 +317,36 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     }
 }
 
-// Merge of the chunks and the rotation back: one wave per (bank, query). Every global read
-// is issued before the first wait: the rotation R_g (direct-to-LDS), the chunk maxima and
-// weight sums, and the partial rows of the first 64 chunks (two coordinates per lane).
-// The chunk maxima (base-2 units) give factors 2^(max_c - max);
-// o_rot = sum_c factor_c o_rot_c / sum_c factor_c sum_c in fp64, and then
+// Merge of the chunks and the rotation back: one work-group of AT_MERGE_WAVES waves per
+// (bank, query). Every wave reads all chunk maxima and weight sums (so each holds the same
+// global maximum and total) and the partial rows of its own chunks c = AT_MERGE_WAVES i + wave
+// (two coordinates per lane), each pass's reads issued before its first wait, beside its share
+// of the rotation R_g (direct-to-LDS). The chunk maxima (base-2 units) give factors
+// 2^(max_c - max); the waves' sums of factor_c o_rot_c add in LDS in wave order (fp64);
+// o_rot = that / sum_c factor_c sum_c; then thread k forms
 // out[chan[off_g + k]] = sum_j R_g[j][k] o_rot[off_g + j]. out [bank][G][d] float32.
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ part, int chunks,
-                                                         const float *__restrict__ rot, const int *__restrict__ chan,
-                                                         AttnArgs a, float *__restrict__ out) {
+constexpr int AT_MERGE_WAVES = 4;
+
+__global__ __launch_bounds__(AT_MERGE_WAVES * 64) void attn_combine_kernel(const float *__restrict__ part, int chunks,
+                                                                          const float *__restrict__ rot,
+                                                                          const int *__restrict__ chan, AttnArgs a,
+                                                                          float *__restrict__ out) {
+    constexpr int MW = AT_MERGE_WAVES, PER = 64 / MW;  // a wave's chunks in a pass of 64
     __shared__ __align__(16) float s_R[AT_DMAX * AT_DMAX];
+    __shared__ double s_v[MW][AT_DMAX];
     __shared__ double s_o[AT_DMAX];
-    const int lane = threadIdx.x, d = a.d, PS = 2 + d;
+    const int tid = threadIdx.x, lane = tid & 63, d = a.d, PS = 2 + d;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const float *pq = part + (size_t)blockIdx.x * chunks * PS;
     // the rotation blocks, back to back: d_0^2 (+ d_1^2) floats, a multiple of 256
     const int nR = a.gdim[0] * a.gdim[0] + (a.ng > 1 ? a.gdim[1] * a.gdim[1] : 0);
-    for (int i = 0; i < nR / 256; ++i)
+    for (int i = wv; i < nR / 256; i += MW)
         __builtin_amdgcn_global_load_lds(rot + 256 * i + 4 * lane, (at_lds_void *)&s_R[256 * i], 16, 0, 0);
     const int k0 = min(lane, d - 1), k1 = min(lane + 64, d - 1);  // clamped reads; results unused
-    float pv0[64], pv1[64];
+    float pv0[PER], pv1[PER];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const float *pr = pq + (size_t)min(i, chunks - 1) * PS + 2;
+    for (int i = 0; i < PER; ++i) {
+        const float *pr = pq + (size_t)min(MW * i + wv, chunks - 1) * PS + 2;
         pv0[i] = pr[k0];
         pv1[i] = pr[k1];
     }
@@ -359,8 +367,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restric
             f = cb + lane < chunks ? pq[(size_t)c * PS] : -INFINITY;
             e = pq[(size_t)c * PS + 1];
 #pragma unroll
-            for (int i = 0; i < 64; ++i) {
-                const float *pr = pq + (size_t)min(cb + i, chunks - 1) * PS + 2;
+            for (int i = 0; i < PER; ++i) {
+                const float *pr = pq + (size_t)min(cb + MW * i + wv, chunks - 1) * PS + 2;
                 pv0[i] = pr[k0];
                 pv1[i] = pr[k1];
             }
@@ -368,21 +376,27 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restric
         f = __builtin_amdgcn_exp2f(f - mx);  // 0 past the last chunk
         tot += (double)f * (double)e;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const double fi = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i));
+        for (int i = 0; i < PER; ++i) {
+            const double fi = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), MW * i + wv));
             v0 += fi * (double)pv0[i];
             v1 += fi * (double)pv1[i];
         }
     }
-    tot = at_wave_sum(tot);
+    tot = at_wave_sum(tot);  // the same in every wave
     if (mx == -INFINITY) tot = 0.0, v0 = v1 = 0.0;  // no key took part: the output is 0
-    s_o[lane] = tot > 0.0 ? v0 / tot : 0.0;
-    s_o[lane + 64] = tot > 0.0 ? v1 / tot : 0.0;
-    __builtin_amdgcn_s_waitcnt(AT_WAIT_VM0);  // the rotation is in LDS
-    __builtin_amdgcn_s_barrier();
-    for (int h = 0; h < 2; ++h) {
-        const int k = lane + 64 * h;
-        if (k >= d) continue;
+    s_v[wv][lane] = v0;
+    s_v[wv][lane + 64] = v1;
+    __builtin_amdgcn_s_waitcnt(AT_WAIT_VM0);  // this wave's share of the rotation is in LDS
+    __syncthreads();
+    if (tid < AT_DMAX) {
+        double v = 0.0;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) v += s_v[w][tid];
+        s_o[tid] = tot > 0.0 ? v / tot : 0.0;
+    }
+    __syncthreads();
+    const int k = tid;
+    if (k < d) {
         const bool g1 = a.ng > 1 && k >= a.gdim[0];
         const int dg = g1 ? a.gdim[1] : a.gdim[0], off = g1 ? a.goff[1] : 0, kk = k - off;
         const float *R = s_R + (g1 ? a.gdim[0] * a.gdim[0] : 0) + kk;

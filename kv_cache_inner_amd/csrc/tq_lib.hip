@@ -1008,7 +1008,8 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
     else
         half_norms(vp) ? chunk_kernel(attn_chunk_kernel<2, true>) : chunk_kernel(attn_chunk_kernel<2, false>);
     if ((rc = launch_status())) return rc;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(64), 0, st, part, (int)chunks, vp->rot,
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(AT_MERGE_WAVES * 64), 0, st, part,
+                       (int)chunks, vp->rot,
                        vp->group_chan, a, out);
     return launch_status();
 }
