@@ -19,7 +19,11 @@
 
 namespace tq {
 
-constexpr int LDS_WAVES = 16;
+// Each operand fragment read from LDS feeds the MFMAs of LDS_TB key tiles: with one tile per
+// read the LDS bandwidth (128 B/clk per CU) bounds the kernel at half the int8 MFMA rate. Two
+// tiles in flight take 256 VGPRs, so a work-group has 8 waves (two per SIMD).
+constexpr int LDS_WAVES = 8;
+constexpr int LDS_TB = 2;
 
 // row tiles of operands a work-group holds in LDS (fragments and constants in ~150 KiB)
 template <class L>
@@ -116,7 +120,8 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
     const int per = (c1 - c0 + LDS_WAVES - 1) / LDS_WAVES;
     const int t0 = min(c0 + wv * per, c1), t1 = min(t0 + per, c1);
     const long n_pad = (long)n_tiles * 16;
-    TileStream<L, 1, 1> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
+    constexpr int TB = LDS_TB;
+    TileStream<L, 1, TB> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
                            rnorms + (size_t)bank * n_pad, nullptr, n, G, t0, t1};
     ts.init_lane();
     float *ob = TOPK ? nullptr : scores + (size_t)bank * G * n;
@@ -130,24 +135,32 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
         li[e] = INT32_MAX;
     }
 
-    TileBatch<L, 1> A, B;
+    TileBatch<L, TB> A, B;
     if (t0 < t1) ts.load(A, t0);
-    for (int t = t0; t < t1; ++t) {
-        if (t + 1 < t1) ts.load(B, t + 1);
-        i32x4 acc[RQ][L::NCLS];
+    for (int t = t0; t < t1; t += TB) {
+        if (t + TB < t1) ts.load(B, t + TB);
+        i32x4 acc[TB][RQ][L::NCLS];
 #pragma unroll
-        for (int rt = 0; rt < RQ; ++rt)
+        for (int u = 0; u < TB; ++u)
 #pragma unroll
-            for (int c = 0; c < L::NCLS; ++c) acc[rt][c] = i32x4{0, 0, 0, 0};
+            for (int rt = 0; rt < RQ; ++rt)
+#pragma unroll
+                for (int c = 0; c < L::NCLS; ++c) acc[u][rt][c] = i32x4{0, 0, 0, 0};
         static_for<L::NQ>([&](auto qc) {
             constexpr int qd = decltype(qc)::value;
             constexpr int nx = L::quad_nx(qd);
-            uint32_t der = A.sw[0][L::quad_sq(qd, 0)];
-            if constexpr (nx > 1) der ^= A.sw[0][L::quad_sq(qd, 1)];
-            if constexpr (nx > 2) der ^= A.sw[0][L::quad_sq(qd, 2)];
+            uint32_t der[TB];
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                der[u] = A.sw[u][L::quad_sq(qd, 0)];
+                if constexpr (nx > 1) der[u] ^= A.sw[u][L::quad_sq(qd, 1)];
+                if constexpr (nx > 2) der[u] ^= A.sw[u][L::quad_sq(qd, 2)];
+            }
             static_for<2>([&](auto hc) {
                 constexpr int h = decltype(hc)::value;
-                const i8x16 b = expand_half<h>(der);
+                i8x16 b[TB];
+#pragma unroll
+                for (int u = 0; u < TB; ++u) b[u] = expand_half<h>(der[u]);
                 static_for<L::NCLS>([&](auto cc) {
                     constexpr int c = decltype(cc)::value;
                     if constexpr (L::quad_has(qd, c)) {
@@ -155,7 +168,9 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
 #pragma unroll
                         for (int rt = 0; rt < RQ; ++rt) {
                             const i8x16 a = *reinterpret_cast<const i8x16 *>(&fa[rt][f][lane][0]);
-                            acc[rt][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[rt][c], 0, 0, 0);
+#pragma unroll
+                            for (int u = 0; u < TB; ++u)
+                                acc[u][rt][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[u], acc[u][rt][c], 0, 0, 0);
                         }
                     }
                 });
@@ -164,7 +179,10 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
             // once would exceed the register budget)
             asm volatile("" ::: "memory");
         });
-        const long key = (long)t * 16 + j;
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+        if (t + u >= t1) break;
+        const long key = (long)(t + u) * 16 + j;
         const bool key_live = key < n;
 #pragma unroll
         for (int rt = 0; rt < RQ; ++rt) {
@@ -172,8 +190,8 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
             static_for<L::NCLS>([&](auto cc) {
                 constexpr int c = decltype(cc)::value;
                 constexpr int g = c < L::NG ? c : 0;
-                const double s = c < L::NG ? (double)A.nu[0][g] : (double)A.rho[0];
-                est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[rt][c]), cs[rt][c], ck[rt][c]), est);
+                const double s = c < L::NG ? (double)A.nu[u][g] : (double)A.rho[u];
+                est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[u][rt][c]), cs[rt][c], ck[rt][c]), est);
             });
             const float e = (float)est;
             const int gq = 4 * (rt0 + rt) + gl;
@@ -185,6 +203,7 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
             } else {
                 if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
             }
+        }
         }
         A = B;
     }
