@@ -370,6 +370,209 @@ def test_zero_key_contributes_nothing():
 
 
 # ------------------------------------------------------------------------------------
+# two permuted channel groups (tambur.pub article: mixed bit widths per channel, the
+# 3.5 / 2.5 bits-per-channel paragraph), and the pair scorer the full-size checks use
+# ------------------------------------------------------------------------------------
+
+def _np_unpack(spec, bits, n):
+    """Bucket indices [n, d] (group order) and sign bits [n, m] read straight from the
+    packed words with numpy: key i is lane i % 16 of tile i // 16; for group g the
+    plane-p word of coordinate j is word0_g + p * d_g / 32 + j // 32, bit j % 32; the
+    sign words follow the code words."""
+    b = np.asarray(bits, np.uint32)
+    keys = np.arange(n)
+    tile, lane = keys // 16, keys % 16
+    codes = np.zeros((n, spec.d), np.int64)
+    off = word0 = 0
+    for dg, bg in spec.groups:
+        for j in range(dg):
+            for p in range(bg):
+                w = b[tile, word0 + p * (dg // 32) + j // 32, lane]
+                codes[:, off + j] |= ((w >> np.uint32(j % 32)) & np.uint32(1)).astype(np.int64) << p
+        word0 += bg * (dg // 32)
+        off += dg
+    signs = np.zeros((n, spec.m), np.uint8)
+    for i in range(spec.m):
+        w = b[tile, word0 + i // 32, lane]
+        signs[:, i] = (w >> np.uint32(i % 32)) & np.uint32(1)
+    return codes, signs
+
+
+def _longctx_split(seed, m=128, d0=32, b0=2, d1=96, b1=1):
+    """Parameters of the long-context layout (32 channels with a 2-bit codebook, 96 with
+    a 1-bit one, one sign sketch over all 128) on a random channel permutation."""
+    g = np.random.default_rng(seed)
+    d = d0 + d1
+    chan = g.permutation(d).astype(np.int32)
+    spec = oracle.Spec(d, m, [(d0, b0), (d1, b1)], chan)
+    gs = [g.standard_normal((d0, d0)).astype(np.float32), g.standard_normal((d1, d1)).astype(np.float32)]
+    S = g.standard_normal((max(m, 1), d)).astype(np.float32) if m else None
+    return spec, gs, S, chan, g
+
+
+def _np_decode(prm, codes, norms, chan):
+    """x_hat in channel order: group g's (nu_g / sqrt(d_g)) R_g^T c_g[idx_g] scattered to
+    the channels the list gives that group (numpy, from the pinned rotation and codebook)."""
+    n = codes.shape[0]
+    d = prm.spec.d
+    out = np.zeros((n, d))
+    off = 0
+    for gi, (dg, bg) in enumerate(prm.spec.groups):
+        c = oracle.codebook(bg)[0]
+        R = prm.rots[gi]
+        yhat = c[codes[:, off:off + dg]]                      # [n, d_g] rotated reconstruction
+        xg = (yhat @ R) * (norms[:n, gi].astype(np.float64) / math.sqrt(dg))[:, None]
+        out[:, chan[off:off + dg]] = xg
+        off += dg
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_two_group_decode_is_the_scatter_of_each_groups_reconstruction(seed):
+    spec, gs, S, chan, g = _longctx_split(40 + seed)
+    prm = oracle.Params(spec, gs, S)
+    n = 37
+    x = (g.standard_normal((n, spec.d)) * g.uniform(0.2, 4, (n, 1))).astype(np.float32)
+    x[:, chan[:32]] *= 8.0                                    # outlier group, as in the workload
+    bits, norms, rnorms = oracle.encode(prm, x)
+    codes, signs = _np_unpack(spec, bits, n)
+    c2, s2 = oracle.unpack(spec, bits, n)
+    np.testing.assert_array_equal(codes, c2)
+    np.testing.assert_array_equal(signs, s2)
+    # norms per group over the channels the list assigns it
+    xd = x.astype(np.float64)
+    np.testing.assert_allclose(norms[:n, 0], np.linalg.norm(xd[:, chan[:32]], axis=1), rtol=1e-7)
+    np.testing.assert_allclose(norms[:n, 1], np.linalg.norm(xd[:, chan[32:]], axis=1), rtol=1e-7)
+    # codes: nearest centroid of the unit-variance rotated coordinates of each group
+    off = 0
+    for gi, (dg, bg) in enumerate(spec.groups):
+        z = math.sqrt(dg) * (xd[:, chan[off:off + dg]] @ prm.rots[gi].T) / np.linalg.norm(
+            xd[:, chan[off:off + dg]], axis=1, keepdims=True)
+        c = oracle.codebook(bg)[0]
+        near = np.argmin(np.abs(z[..., None] - c), axis=-1)
+        clear = np.min(np.abs(z[..., None] - oracle.codebook(bg)[1]), axis=-1) > 1e-9 if bg > 0 else True
+        np.testing.assert_array_equal(codes[:, off:off + dg][clear], near[clear])
+        off += dg
+    # decode against the numpy scatter
+    np.testing.assert_allclose(oracle.decode(prm, bits, norms, n), _np_decode(prm, codes, norms, chan),
+                               rtol=0, atol=1e-12 * np.abs(xd).max())
+    # the residual: its norm and signs are those of x - decode(bytes), S in channel order
+    r = xd - _np_decode(prm, codes, norms, chan)
+    np.testing.assert_allclose(rnorms[:n], np.linalg.norm(r, axis=1), rtol=1e-6)
+    p = r @ S.astype(np.float64).T
+    clear = np.abs(p) > 1e-9 * np.abs(p).max()
+    np.testing.assert_array_equal(signs[clear], (p[clear] >= 0).astype(np.uint8))
+
+
+def test_two_group_encoding_is_equivariant_under_channel_relabelling():
+    """Encoding x with channel list chan equals encoding x[chan] (groups now contiguous)
+    with the identity list and S's columns taken in the same order: a scatter through the
+    inverse list, or a residual or projection in the wrong channel order, breaks it."""
+    spec, gs, S, chan, g = _longctx_split(47)
+    n = 50
+    x = g.standard_normal((n, spec.d)).astype(np.float32)
+    b1, n1, r1, z1, p1 = oracle.encode_trace(oracle.Params(spec, gs, S), x)
+    spec_id = oracle.Spec(spec.d, spec.m, spec.groups, None)
+    b2, n2, r2, z2, p2 = oracle.encode_trace(oracle.Params(spec_id, gs, np.ascontiguousarray(S[:, chan])),
+                                             np.ascontiguousarray(x[:, chan]))
+    c1, s1 = oracle.unpack(spec, b1, n)
+    c2, s2 = oracle.unpack(spec_id, b2, n)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(n1, n2)
+    np.testing.assert_allclose(z1, z2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r1, r2, rtol=1e-7)
+    np.testing.assert_allclose(p1, p2, rtol=0, atol=1e-10 * np.abs(p1).max())
+    clear = np.abs(p1) > 1e-9 * np.abs(p1).max()
+    np.testing.assert_array_equal(s1[clear], s2[clear])
+    # and the relabelled list does matter: the identity list on the unpermuted keys differs
+    b3, _, _ = oracle.encode(oracle.Params(spec_id, gs, S), x)
+    assert (oracle.unpack(spec_id, b3, n)[0] != c1).any()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_two_group_mse_only_score_is_the_inner_product_with_the_decode(seed):
+    spec, gs, _, chan, g = _longctx_split(60 + seed, m=0)
+    prm = oracle.Params(spec, gs, None)
+    n = 41
+    x = g.standard_normal((n, spec.d)).astype(np.float32)
+    bits, norms, rnorms = oracle.encode(prm, x)
+    q = g.standard_normal((5, spec.d)).astype(np.float32)
+    codes, _ = _np_unpack(spec, bits, n)
+    ref = q.astype(np.float64) @ _np_decode(prm, codes, norms, chan).T
+    np.testing.assert_allclose(oracle.score(prm, bits, norms, rnorms, n, q), ref, rtol=1e-11, atol=1e-11)
+
+
+def test_two_group_sketch_term_is_the_signed_projection_sum():
+    """est - <q, x_hat> is sqrt(pi/2)/m * rho * <S q, 2 s - 1> with S q taken over the
+    original channel order (a query read in group order would differ)."""
+    spec, gs, S, chan, g = _longctx_split(70, m=64)
+    prm = oracle.Params(spec, gs, S)
+    n = 23
+    x = g.standard_normal((n, spec.d)).astype(np.float32)
+    bits, norms, rnorms = oracle.encode(prm, x)
+    q = g.standard_normal((3, spec.d)).astype(np.float32)
+    codes, signs = _np_unpack(spec, bits, n)
+    qd = q.astype(np.float64)
+    mse = qd @ _np_decode(prm, codes, norms, chan).T
+    qs = qd @ S.astype(np.float64).T                                     # [G, m]
+    sk = math.sqrt(math.pi / 2) / spec.m * rnorms[:n].astype(np.float64) * (qs @ (2.0 * signs - 1).T)
+    np.testing.assert_allclose(oracle.score(prm, bits, norms, rnorms, n, q), mse + sk, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("two_groups", [False, True])
+def test_score_pairs_is_the_score_matrix_entry(two_groups):
+    """The pair scorer (used by the full-size checks) returns score[qi, ki] exactly, with
+    m different from d so that an offset by d instead of m in the projected query shows."""
+    g = np.random.default_rng(80 + two_groups)
+    if two_groups:
+        spec, gs, S, chan, _ = _longctx_split(81, m=96)
+    else:
+        spec = oracle.Spec(64, 160, [(64, 3)])
+        gs, S = [g.standard_normal((64, 64)).astype(np.float32)], g.standard_normal((160, 64)).astype(np.float32)
+    prm = oracle.Params(spec, gs, S)
+    n, G = 45, 7
+    x = g.standard_normal((n, spec.d)).astype(np.float32)
+    bits, norms, rnorms = oracle.encode(prm, x)
+    q = g.standard_normal((G, spec.d)).astype(np.float32)
+    full = oracle.score(prm, bits, norms, rnorms, n, q)
+    qi = g.integers(0, G, 400)
+    ki = g.integers(0, n, 400)
+    qi[:2], ki[:2] = [0, G - 1], [n - 1, 0]
+    got = oracle.score_pairs(prm, bits, norms, rnorms, q, qi, ki)
+    np.testing.assert_array_equal(got, full[qi, ki])
+
+
+@pytest.mark.slow
+def test_two_group_estimator_unbiased_over_projections_and_rotations():
+    g = np.random.default_rng(91)
+    d = 128
+    chan = g.permutation(d).astype(np.int32)
+    spec = oracle.Spec(d, d, [(32, 2), (96, 1)], chan)
+    x = g.standard_normal(d).astype(np.float32)
+    x[chan[:32]] *= 8.0
+    q = (x / 4 + g.standard_normal(d)).astype(np.float32)
+    truth = float(q.astype(np.float64) @ x.astype(np.float64))
+    vals = np.empty(1500)
+    for s in range(len(vals)):
+        h = np.random.default_rng(11000 + s)
+        prm = oracle.Params(spec, [h.standard_normal((32, 32)).astype(np.float32),
+                                   h.standard_normal((96, 96)).astype(np.float32)],
+                            h.standard_normal((d, d)).astype(np.float32))
+        b_, n_, r_ = oracle.encode(prm, x[None])
+        vals[s] = oracle.score(prm, b_, n_, r_, 1, q[None])[0, 0]
+    assert abs(vals.mean() - truth) < 4 * vals.std(ddof=1) / math.sqrt(len(vals))
+    # over projections alone (rotations fixed): the MSE part is fixed, the sketch unbiased
+    h = np.random.default_rng(12)
+    gs = [h.standard_normal((32, 32)).astype(np.float32), h.standard_normal((96, 96)).astype(np.float32)]
+    prm = oracle.Params(spec, gs, np.zeros((d, d), np.float32))
+    for s in range(len(vals)):
+        prm.proj = np.random.default_rng(13000 + s).standard_normal((d, d)).astype(np.float32)
+        b_, n_, r_ = oracle.encode(prm, x[None])
+        vals[s] = oracle.score(prm, b_, n_, r_, 1, q[None])[0, 0]
+    assert abs(vals.mean() - truth) < 4 * vals.std(ddof=1) / math.sqrt(len(vals))
+
+
+# ------------------------------------------------------------------------------------
 # distortion (turboquant-pytorch write-up, performance section: 0.034 measured, 0.043 bound)
 # ------------------------------------------------------------------------------------
 
