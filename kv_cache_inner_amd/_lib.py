@@ -108,6 +108,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Context in which the binding allocates a call's workspace and outputs: the launch
+    stream, so that torch's caching allocator orders any later reuse of those blocks after
+    the kernels that use them (a block freed on another stream could be handed out while
+    the kernels still run)."""
+    import contextlib
+
+    import torch
+
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 # ------------------------------------------------------------------------------------------
 # host-only entry points
 # ------------------------------------------------------------------------------------------
@@ -231,7 +243,8 @@ def _workspace(nbytes: int, device):
 
 
 # ------------------------------------------------------------------------------------------
-# device entry points (asynchronous on the current torch stream unless one is given)
+# device entry points (asynchronous on the current torch stream unless one is given; the
+# workspace and outputs a call allocates itself are allocated on the launch stream)
 # ------------------------------------------------------------------------------------------
 
 def tq_encode(params: Params, keys, bank: Bank, workspace=None, stream=None):
@@ -242,7 +255,8 @@ def tq_encode(params: Params, keys, bank: Bank, workspace=None, stream=None):
     assert keys.dtype in (torch.bfloat16, torch.float32)
     banks, n = keys.shape[0], keys.shape[1]
     ws_bytes = params.workspace_bytes(TQ_OP_ENCODE, banks, n)
-    ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
+    with _on(stream):
+        ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
     _check("tq_encode", _lib.tq_encode(params.ref, keys.data_ptr(), dtype, banks, n, bank.ref, ws.data_ptr(),
                                        ws.numel(), _stream(stream)))
     return bank
@@ -260,7 +274,8 @@ def tq_encode_append(params: Params, keys, bank: Bank, pos, workspace=None, prep
     dtype = TQ_BF16 if keys.dtype == torch.bfloat16 else TQ_F32
     banks, count = keys.shape[0], keys.shape[1]
     ws_bytes = params.workspace_bytes(TQ_OP_ENCODE, banks, count)
-    ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
+    with _on(stream):
+        ws = workspace if workspace is not None else _workspace(ws_bytes, keys.device)
     _check("tq_encode_append", _lib.tq_encode_append(params.ref, keys.data_ptr(), dtype, banks, count, pos.data_ptr(),
                                                      bank.n, bank.ref, TQ_APPEND_PREPARED if prepared else 0,
                                                      ws.data_ptr(), ws.numel(), _stream(stream)))
@@ -288,9 +303,10 @@ def tq_score(params: Params, bank: Bank, q, scores=None, workspace=None, stream=
 
     assert q.is_contiguous() and q.dim() == 3 and q.shape[0] == bank.banks and q.shape[2] == params.d
     G = q.shape[1]
-    if scores is None:
-        scores = torch.empty((bank.banks, G, bank.n), dtype=torch.float32, device=q.device)
-    ws = workspace if workspace is not None else score_workspace(params, bank, G)
+    with _on(stream):
+        if scores is None:
+            scores = torch.empty((bank.banks, G, bank.n), dtype=torch.float32, device=q.device)
+        ws = workspace if workspace is not None else score_workspace(params, bank, G)
     _check("tq_score", _lib.tq_score(params.ref, bank.ref, bank.banks, bank.n, q.data_ptr(), G, scores.data_ptr(),
                                      ws.data_ptr(), ws.numel(), _stream(stream)))
     return scores
@@ -301,10 +317,11 @@ def tq_topk(params: Params, bank: Bank, q, k: int, workspace=None, stream=None):
 
     assert q.is_contiguous() and q.dim() == 3 and q.shape[0] == bank.banks and q.shape[2] == params.d
     G = q.shape[1]
-    vals = torch.empty((bank.banks, G, k), dtype=torch.float32, device=q.device)
-    idx = torch.empty((bank.banks, G, k), dtype=torch.int32, device=q.device)
-    ws = workspace if workspace is not None else _workspace(
-        params.workspace_bytes(TQ_OP_TOPK, bank.banks, bank.n, G, k), q.device)
+    with _on(stream):
+        vals = torch.empty((bank.banks, G, k), dtype=torch.float32, device=q.device)
+        idx = torch.empty((bank.banks, G, k), dtype=torch.int32, device=q.device)
+        ws = workspace if workspace is not None else _workspace(
+            params.workspace_bytes(TQ_OP_TOPK, bank.banks, bank.n, G, k), q.device)
     _check("tq_topk", _lib.tq_topk(params.ref, bank.ref, bank.banks, bank.n, q.data_ptr(), G, k, vals.data_ptr(),
                                    idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
     return vals, idx
@@ -315,7 +332,8 @@ def tq_decode(params: Params, bank: Bank, out=None, stream=None):
     import torch
 
     if out is None:
-        out = torch.empty((bank.banks, bank.n, params.d), dtype=torch.float32, device=bank.bits.device)
+        with _on(stream):
+            out = torch.empty((bank.banks, bank.n, params.d), dtype=torch.float32, device=bank.bits.device)
     _check("tq_decode", _lib.tq_decode(params.ref, bank.ref, bank.banks, bank.n, out.data_ptr(), _stream(stream)))
     return out
 
@@ -337,9 +355,10 @@ def tq_attend(kparams: Params, kbank: Bank, vparams: Params, vbank: Bank, q, sca
     if lengths is not None:
         assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.numel() == kbank.banks
     G = q.shape[1]
-    if out is None:
-        out = torch.empty((kbank.banks, G, vparams.d), dtype=torch.float32, device=q.device)
-    ws = workspace if workspace is not None else attend_workspace(kparams, kbank, G)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((kbank.banks, G, vparams.d), dtype=torch.float32, device=q.device)
+        ws = workspace if workspace is not None else attend_workspace(kparams, kbank, G)
     _check("tq_attend", _lib.tq_attend(kparams.ref, kbank.ref, vparams.ref, vbank.ref, kbank.banks, kbank.n,
                                        _ptr(lengths), q.data_ptr(), G, float(scale), out.data_ptr(), ws.data_ptr(),
                                        ws.numel(), _stream(stream)))
@@ -352,7 +371,8 @@ def tq_fp32_logits(keys, q, scores=None, stream=None):
     banks, n, d = keys.shape
     G = q.shape[1]
     if scores is None:
-        scores = torch.empty((banks, G, n), dtype=torch.float32, device=keys.device)
+        with _on(stream):
+            scores = torch.empty((banks, G, n), dtype=torch.float32, device=keys.device)
     _check("tq_fp32_logits", _lib.tq_fp32_logits(keys.data_ptr(), banks, n, d, q.data_ptr(), G, scores.data_ptr(),
                                                  _stream(stream)))
     return scores

@@ -863,6 +863,7 @@ extern "C" int tq_topk(const tq_params *p, const tq_bank *in, int64_t banks, int
     if (p->m == 0) return TQ_ERR_UNSUPPORTED;  // the estimator needs the sign sketch
     if (banks < 0 || n < 0 || G < 1 || k < 1 || k > 64 || k > n) return TQ_ERR_ARG;
     if (banks == 0) return TQ_OK;
+    if (n > INT32_MAX) return TQ_ERR_UNSUPPORTED;  // key indices are returned as int32
     if (!in || !in->bits || !in->norms || !in->rnorms || !q || !vals || !idx || bank_misaligned(in)) return TQ_ERR_ARG;
     if (!workspace || ((uintptr_t)workspace & 255)) return TQ_ERR_WORKSPACE;
     if (ws_bytes < tq_workspace_bytes(TQ_OP_TOPK, p, banks, n, G, k)) return TQ_ERR_WORKSPACE;

@@ -159,6 +159,50 @@ def test_topk_full_search_sampled(tq, bits):
         say(f"   query {qi}: overlap with the oracle's top-{k} {same:.2f}")
 
 
+def _sample_rows(n, chunk, count, seed):
+    """Rows to check in a bank of n keys: the first and last, both sides of every
+    residual-chunk boundary of the large-key encoder, then seeded random rows up to
+    `count` (a multiple of 16), sorted."""
+    rows = {0, n - 1}
+    for b in range(chunk, n, chunk):
+        rows.update((b - 1, b))
+    g = np.random.default_rng(seed)
+    while len(rows) < count:
+        rows.update(g.integers(0, n, count - len(rows)).tolist())
+    return np.array(sorted(rows)[:count], np.int64)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_encode_full_search_sampled(tq, bits):
+    """The full 2,000,000 x 768 search database encoded by the GPU (the launch sequence the
+    benchmark times: 62 residual chunks of 32768 rows); 2048 rows, including the first, the
+    last and both sides of every chunk boundary, re-encoded by the oracle and compared
+    record by record (codes within the decision band, signs, norms)."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    n = cfg.tokens
+    say(f"encode full search b={bits}: {n} x {cfg.d}")
+    gpu, orc = both_params(cfg, bits)
+    keys = workloads.keys_device(cfg, 0, "cuda")
+    bank = tq.Bank(gpu, 1, n)
+    tq.tq_encode(gpu, keys, bank)
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, 32768, 2048, 500 + bits)
+    assert len(rows) == 2048 and rows[0] == 0 and rows[-1] == n - 1
+    r = torch.from_numpy(rows).cuda()
+    # the sampled records gathered into a compact bank of 2048 keys (128 whole tiles)
+    W = bank.W
+    sb = bank.bits[0][r // 16, :, r % 16].reshape(128, 16, W).permute(0, 2, 1).contiguous()
+    sub = (sb.cpu().numpy().view(np.uint32), bank.norms[0][r].cpu().numpy(), bank.rnorms[0][r].cpu().numpy())
+    kh = keys[0][r].cpu().numpy()
+    del keys, bank
+    torch.cuda.empty_cache()
+    rep = {}
+    check_encode(sub, oracle.encode_trace(orc, kh), orc, len(rows), rep)
+    say("   report", rep)
+
+
 # ------------------------------------------------------------------------------------------
 # encoder for keys above 128 dimensions (tiled two-GEMM path): partial tiles, two channel
 # groups with a channel permutation, bf16 and fp32 keys, several residual chunks
@@ -208,3 +252,42 @@ def test_encode_large_keys_several_chunks(tq):
     keys = workloads.keys(cfg, n=11111, banks=[0, 1, 2])
     say("encode large keys, 3 x 11111 keys (two residual chunks)")
     say("   report", _encode_vs_oracle(tq, cfg, 3, keys))
+
+
+@pytest.mark.parametrize("op", ["topk", "score"])
+def test_side_stream_results_survive_default_stream_allocations(tq, op):
+    """A call on a side stream allocates its workspace and outputs on that stream: memory
+    the default stream allocates and overwrites while the kernels still run must not be
+    the call's workspace (a block freed to the current stream's pool could be)."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    n, G, k, bits = 60000, 40, 10, 4
+    say(f"side stream {op}: d=768 b={bits} n={n} G={G}")
+    keys = workloads.keys(cfg, n=n)
+    q = workloads.queries(cfg, G=G)
+    gpu, orc, refs, bank = _oracle_bank(tq, cfg, bits, keys)
+    qd = torch.from_numpy(q).cuda()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ws_bytes = gpu.workspace_bytes(tq.TQ_OP_TOPK if op == "topk" else tq.TQ_OP_SCORE, 1, n, G, k)
+    outs = []
+    for rep in range(3):
+        if op == "topk":
+            outs.append(tq.tq_topk(gpu, bank, qd, k, stream=side))
+        else:
+            outs.append((tq.tq_score(gpu, bank, qd, stream=side),))
+        # while the side stream runs: allocate and scribble on the default stream
+        for _ in range(4):
+            junk = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+            junk.fill_(0xA5)
+            junk2 = torch.empty((1, G, max(k, n)), dtype=torch.float32, device="cuda")
+            junk2.fill_(-1e30)
+            del junk, junk2
+    torch.cuda.synchronize()
+    ref = oracle.score(orc, *refs[0], n, q[0])
+    for o in outs:
+        if op == "topk":
+            check_topk(o[0].cpu().numpy()[0], o[1].cpu().numpy()[0], ref, k)
+        else:
+            check_scores(o[0].cpu().numpy()[0], ref)

@@ -194,6 +194,12 @@ def test_argument_validation_returns_before_any_launch(tq):
                      None) == tq.TQ_ERR_WORKSPACE
     assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4001, 1 << 20,
                      None) == tq.TQ_ERR_WORKSPACE
+    # top-k returns int32 key indices: a bank of more than INT32_MAX keys is refused
+    # (about 155 GB at d = 128, b = 3: it would fit in device memory)
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, 1 << 31, 0x1000, 4, 10, 0x2000, 0x3000, 0x4000, 1 << 40,
+                     None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_topk(good.ref, ctypes.byref(bank), 1, (1 << 31) - 1, 0x1000, 4, 10, 0x2000, 0x3000, 0x4000, 64,
+                     None) == tq.TQ_ERR_WORKSPACE
     # append: null keys or positions, negative sizes, bad dtype, small or misaligned workspace
     A = L.tq_encode_append
     assert A(good.ref, None, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
