@@ -23,7 +23,8 @@
  *   - Returns TQ_OK (0) or a negative tq_status. TQ_ERR_DEVICE reports a failed
  *     launch (the HIP error is not cleared). tq_status_string() names a code.
  *   - Results are bit-identical from run to run for identical inputs.
- *   - Calls are thread-safe; the library holds no mutable global state.
+ *   - Calls are thread-safe. The only state the library keeps is, per device, the
+ *     address of the device array used by tq_encode_append_noalloc (looked up once).
  *   - Non-finite inputs give unspecified (but memory-safe) results.
  *   - The matrices (rot, proj) and the bank arrays read by the scorers, top-k, decode and
  *     attention are read with 16-byte loads: their pointers must be 16-byte aligned
@@ -180,6 +181,21 @@ int tq_encode(const tq_params *p, const void *keys, int dtype, int64_t banks, in
 int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
                      const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
                      size_t ws_bytes, void *stream);
+
+/* Streaming append for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): tq_encode_append with
+ * flags = 0, except that the folded projection S' is formed in a device array the library
+ * holds for the life of the process (one per device, TQ_NOALLOC_SCRATCH_BYTES) instead of in
+ * a caller workspace. The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). Arguments, slots and results as tq_encode_append; layouts with
+ * d > 128 or m > 128 (whose encoder needs more scratch than the array holds):
+ * TQ_ERR_UNSUPPORTED. Every call on a device shares that device's array and re-forms S' in
+ * it, so calls that may overlap on one device (several streams, several host threads) race
+ * and must be serialised by the caller; calls in order on one stream do not. TQ_ERR_DEVICE
+ * if the array's device address cannot be obtained. */
+#define TQ_NOALLOC_SCRATCH_BYTES 65536
+int tq_encode_append_noalloc(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                             const int32_t *pos, int64_t n_cap, const tq_bank *out, void *stream);
 
 /* Query preparation (per query: R_g q_g and S q, once, as the estimator's
  * operands; same write-up, usage example: the query stays at full precision).

@@ -43,7 +43,8 @@ class tq_bank(ctypes.Structure):
 
 
 EXPORTS = ["tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_make_rotation_hadamard",
-           "tq_bank_layout", "tq_workspace_bytes", "tq_encode", "tq_encode_append", "tq_prepare_queries",
+           "tq_bank_layout", "tq_workspace_bytes", "tq_encode", "tq_encode_append", "tq_encode_append_noalloc",
+           "tq_prepare_queries",
            "tq_score_prepared", "tq_score", "tq_topk", "tq_decode", "tq_attend", "tq_fp32_logits", "tq_copy",
            "tq_status_string"]
 
@@ -64,6 +65,7 @@ def _load():
         "tq_workspace_bytes": (sz, [ctypes.c_int, P, i64, i64, i32, i32]),
         "tq_encode": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, B, vp, sz, vp]),
         "tq_encode_append": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, vp, i64, B, ctypes.c_int, vp, sz, vp]),
+        "tq_encode_append_noalloc": (ctypes.c_int, [P, vp, ctypes.c_int, i64, i64, vp, i64, B, vp]),
         "tq_prepare_queries": (ctypes.c_int, [P, vp, i64, i32, vp, sz, vp]),
         "tq_score_prepared": (ctypes.c_int, [P, B, i64, i64, i32, vp, vp, vp]),
         "tq_score": (ctypes.c_int, [P, B, i64, i64, vp, i32, vp, vp, sz, vp]),
@@ -279,6 +281,21 @@ def tq_encode_append(params: Params, keys, bank: Bank, pos, workspace=None, prep
     _check("tq_encode_append", _lib.tq_encode_append(params.ref, keys.data_ptr(), dtype, banks, count, pos.data_ptr(),
                                                      bank.n, bank.ref, TQ_APPEND_PREPARED if prepared else 0,
                                                      ws.data_ptr(), ws.numel(), _stream(stream)))
+    return bank
+
+
+def tq_encode_append_noalloc(params: Params, keys, bank: Bank, pos, stream=None):
+    """tq_encode_append without a workspace: S' is formed in the library's own device array
+    (d, m <= 128). Calls that overlap on one device race (they share that array)."""
+    import torch
+
+    assert keys.is_contiguous() and keys.dim() == 3 and keys.shape[2] == params.d
+    assert keys.dtype in (torch.bfloat16, torch.float32)
+    assert pos.dtype == torch.int32 and pos.is_contiguous() and pos.numel() == keys.shape[0] == bank.banks
+    dtype = TQ_BF16 if keys.dtype == torch.bfloat16 else TQ_F32
+    _check("tq_encode_append_noalloc", _lib.tq_encode_append_noalloc(params.ref, keys.data_ptr(), dtype, keys.shape[0],
+                                                                     keys.shape[1], pos.data_ptr(), bank.n, bank.ref,
+                                                                     _stream(stream)))
     return bank
 
 

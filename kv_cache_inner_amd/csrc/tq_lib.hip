@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/tq.h"
@@ -577,27 +578,32 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     return launch_status();
 }
 
-extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
-                                const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
-                                size_t ws_bytes, void *stream) {
+// Argument checks shared by the two append entry points (nothing is enqueued).
+static int check_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                        const int32_t *pos, int64_t n_cap, const tq_bank *out) {
     int rc = check_params(p);
     if (rc) return rc;
     if (banks < 0 || count < 0 || n_cap < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
-    if (flags & ~TQ_APPEND_PREPARED) return TQ_ERR_ARG;
     if (banks == 0 || count == 0 || n_cap == 0) return TQ_OK;
     if (!keys || !pos || !out || !out->bits || !out->norms || !out->rnorms) return TQ_ERR_ARG;
-    const size_t ws_need = enc_ws_layout(p, banks, count).total;
-    if (ws_need && (!workspace || ws_bytes < ws_need || ((uintptr_t)workspace & 255))) return TQ_ERR_WORKSPACE;
     const int64_t n_tiles = (count + 15) / 16, cap_tiles = (n_cap + 15) / 16;
     if (banks * n_tiles > INT32_MAX || cap_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
-    const size_t smem = enc_smem_bytes(p->d, p->m);
-    if (smem > 150 * 1024) return TQ_ERR_UNSUPPORTED;
+    if (enc_smem_bytes(p->d, p->m) > 150 * 1024) return TQ_ERR_UNSUPPORTED;
     const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
     if (half_norms(p) && !split) return TQ_ERR_UNSUPPORTED;  // binary16 norms: the split encoder only
-    hipStream_t st = (hipStream_t)stream;
+    return TQ_OK;
+}
+
+// The launches of an append, arguments already checked: the S' fold into sp (when fold),
+// then the encoder placing each key in its slot.
+static int launch_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                         const int32_t *pos, int64_t n_cap, const tq_bank *out, bool fold, float *sp, hipStream_t st) {
+    int rc;
+    const int64_t n_tiles = (count + 15) / 16, cap_tiles = (n_cap + 15) / 16;
+    const size_t smem = enc_smem_bytes(p->d, p->m);
+    const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
     const EncArgs a = enc_args(p);
-    float *sp = (float *)workspace;
-    if (!(flags & TQ_APPEND_PREPARED)) {
+    if (fold) {
         launch_prep_proj(p, a, sp, st);
         if ((rc = launch_status())) return rc;
     }
@@ -630,6 +636,57 @@ extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype,
                            (float *)out->rnorms, slots);
     }
     return launch_status();
+}
+
+extern "C" int tq_encode_append(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                                const int32_t *pos, int64_t n_cap, const tq_bank *out, int flags, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    int rc = check_append(p, keys, dtype, banks, count, pos, n_cap, out);
+    if (rc) return rc;
+    if (flags & ~TQ_APPEND_PREPARED) return TQ_ERR_ARG;
+    if (banks == 0 || count == 0 || n_cap == 0) return TQ_OK;
+    const size_t ws_need = enc_ws_layout(p, banks, count).total;
+    if (ws_need && (!workspace || ws_bytes < ws_need || ((uintptr_t)workspace & 255))) return TQ_ERR_WORKSPACE;
+    return launch_append(p, keys, dtype, banks, count, pos, n_cap, out, !(flags & TQ_APPEND_PREPARED),
+                         (float *)workspace, (hipStream_t)stream);
+}
+
+// ----------------------------------------------------------------------------------------
+// Append without allocation: the folded projection S' (m x d floats) lives in a file-scope
+// device array instead of a caller workspace. Each device holds its own copy of the array;
+// its device address is looked up once per device (the host-side name is only a handle
+// for that lookup and is never passed to a kernel).
+// ----------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// The current device's address of `scratch`, or nullptr if the lookup fails.
+static void *scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
+extern "C" int tq_encode_append_noalloc(const tq_params *p, const void *keys, int dtype, int64_t banks, int64_t count,
+                                        const int32_t *pos, int64_t n_cap, const tq_bank *out, void *stream) {
+    int rc = check_append(p, keys, dtype, banks, count, pos, n_cap, out);
+    if (rc) return rc;
+    // the layouts whose only scratch is S': d, m <= 128, at most 64 KiB
+    if (p->d > ENCS_DMAX || p->m > ENCS_DMAX || (size_t)p->m * p->d * 4 > TQ_NOALLOC_SCRATCH_BYTES)
+        return TQ_ERR_UNSUPPORTED;
+    if (banks == 0 || count == 0 || n_cap == 0) return TQ_OK;
+    float *sp = (float *)scratch_on_current_device();
+    if (!sp) return TQ_ERR_DEVICE;
+    return launch_append(p, keys, dtype, banks, count, pos, n_cap, out, true, sp, (hipStream_t)stream);
 }
 
 static PrepArgs prep_args(const tq_params *p) {

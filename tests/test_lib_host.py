@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol(tq):
     names = _declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(tq.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -212,6 +212,17 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2010, 1 << 20, None) == tq.TQ_ERR_WORKSPACE
     assert A(good.ref, None, 0, 4, 0, None, 100, ctypes.byref(nullbank), 0, None, 0, None) == tq.TQ_OK
     assert A(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), 2, 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
+    # the no-allocation append: the same checks, and layouts beyond its device array refused
+    N = L.tq_encode_append_noalloc
+    assert N(good.ref, None, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), None) == tq.TQ_ERR_ARG
+    assert N(good.ref, 0x1000, 0, 1, 1, None, 100, ctypes.byref(bank), None) == tq.TQ_ERR_ARG
+    assert N(good.ref, 0x1000, 3, 1, 1, 0x6000, 100, ctypes.byref(bank), None) == tq.TQ_ERR_ARG
+    assert N(good.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(nullbank), None) == tq.TQ_ERR_ARG
+    assert N(good.ref, None, 0, 4, 0, None, 100, ctypes.byref(nullbank), None) == tq.TQ_OK
+    for big in (_with_fake_ptrs(tq, d=256, m=128, groups=((256, 2),)),
+                _with_fake_ptrs(tq, d=128, m=256, groups=((128, 2),)),
+                _with_fake_ptrs(tq, d=768, m=768, groups=((768, 3),))):
+        assert N(big.ref, 0x1000, 0, 1, 1, 0x6000, 100, ctypes.byref(bank), None) == tq.TQ_ERR_UNSUPPORTED
     assert L.tq_fp32_logits(None, 1, 10, 128, 0x1000, 4, 0x2000, None) == tq.TQ_ERR_ARG
     assert L.tq_copy(0x1001, 0x2000, 64, None) == tq.TQ_ERR_ARG
     # decompression and attention: value params are MSE-only (m = 0), d_v <= 128
