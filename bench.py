@@ -58,11 +58,18 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the ring scorer is built from: its device code (the scorer, layout
+    and device-helper headers) and its host launch function (grid and arguments)."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_inner_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("tq_device.h", "tq_layout.h", "tq_score.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    lib = open(os.path.join(csrc, "tq_lib.hip")).read()
+    m = re.search(r"static int launch_ring\(.*?\n}\n", lib, re.S)
+    h.update((m.group(0) if m else "").encode())
     return h.hexdigest()[:16]
 
 
@@ -418,6 +425,113 @@ def variants_extra(tq, device):
                                               tq.tq_make_codebook(groups[0][1])[2]]}
 
 
+def fp32_comparator(tq, device, layers, steps, packed_launch_ms):
+    """The fp32 unquantized-keys logits kernel on the decode8b shapes (528 B per key: the 32-bit
+    keys the packed format replaces, and the G = 4 scores), 4 distinct fp32 layers (4.3 GB,
+    far beyond the 256 MB last-level cache) cycled over the sweep's layer count. The speedup
+    of the packed scorer is reported per launch and, beside it, the byte ratio that bounds it
+    when both kernels stream at the same rate."""
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    nfp = 4
+    kf = [workloads.keys_device(cfg, l, device, dtype=torch.float32) for l in range(nfp)]
+    qf = [workloads.queries_device(cfg, l, device) for l in range(nfp)]
+    sf = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
+
+    def fp32_step():
+        for layer in range(layers):
+            tq.tq_fp32_logits(kf[layer % nfp], qf[layer % nfp], sf)
+
+    wallf, kernf = timed(fp32_step, steps, 1, layers)
+    fbytes = cfg.banks * cfg.tokens * (4 * cfg.d + 4 * cfg.G)
+    pbytes = cfg.banks * cfg.tokens * (56 + 4 * cfg.G)
+    del kf
+    return {
+        "value": cfg.banks * cfg.tokens * cfg.G * layers / (wallf / steps),
+        "unit": "pairs/s",
+        "avg_launch_ms": float(np.mean(kernf)),
+        "kernel_gbps": fbytes / (np.mean(kernf) * 1e-3) / 1e9,
+        "speedup_of_packed_b3": float(np.mean(kernf)) / packed_launch_ms,
+        "byte_ratio_b3": fbytes / pbytes,
+        "context": "the pages quote up to 8x for 4-bit keys vs 32-bit keys on H100",
+    }
+
+
+def launch_sweep(tq, device, reps=32):
+    """Launch-size sweep on the decode shapes (64 banks, G = 4, d = 128, b = 3): per launch
+    size, the ring scorer and a plain copy moving the same algorithmic bytes (half read, half
+    written), each cycled over distinct buffers (about 1.2 GB in all, so no launch is served
+    from the 256 MB last-level cache) and timed back to back, as the decode step runs them.
+    A least-squares fit t = t0 + B / BW_inf over the sizes separates the fixed cost of a
+    launch (t0) from its asymptotic streaming rate (BW_inf)."""
+    import ctypes
+
+    import torch
+    import workloads
+
+    cfg = workloads.CONFIGS["decode8b"]
+    prm = params_for(tq, cfg, 3, device)
+    lib = tq._lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    banks, G = cfg.banks, cfg.G
+    sizes = [4096, 8192, 16384, 32768, 65536, 131072]  # keys per bank
+    q = workloads.queries_device(cfg, 0, device)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for n in sizes:
+        W, npad, bpk = prm.layout(n)
+        alg = banks * n * (bpk + 4 * G)
+        copies = max(2, -(-int(1.2e9) // (banks * npad * bpk)))
+        bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (copies * banks, npad // 16, W, 16), dtype=torch.int32,
+                             device=device)
+        norms = torch.rand((copies * banks, npad, 1), device=device) + 0.5
+        rnorms = torch.rand((copies * banks, npad), device=device) * 0.5 + 0.1
+        scores = [torch.empty((banks, G, n), dtype=torch.float32, device=device) for _ in range(2)]
+        structs = [tq.tq_bank(bits[c * banks].data_ptr(), norms[c * banks].data_ptr(), rnorms[c * banks].data_ptr())
+                   for c in range(copies)]
+        calls = [(prm.ref, ctypes.byref(structs[i % copies]), banks, n, q.data_ptr(), G, scores[i % 2].data_ptr(),
+                  None, 0, stream) for i in range(max(reps, copies))]
+        for c in calls[:copies]:
+            assert lib.tq_score(*c) == 0
+        a.record()
+        for c in calls:
+            lib.tq_score(*c)
+        b.record()
+        torch.cuda.synchronize()
+        score_us = a.elapsed_time(b) * 1e3 / len(calls)
+        del bits, norms, rnorms, scores, structs, calls
+        half = (alg // 2 + 15) // 16 * 16
+        cc = max(2, -(-int(1.2e9) // (2 * half)))
+        buf = torch.empty((cc, 2, half), dtype=torch.uint8, device=device)
+        for i in range(cc):
+            tq.tq_copy(buf[i, 0], buf[i, 1])
+        a.record()
+        ncopy = max(reps, cc)
+        for i in range(ncopy):
+            tq.tq_copy(buf[i % cc, 0], buf[i % cc, 1])
+        b.record()
+        torch.cuda.synchronize()
+        copy_us = a.elapsed_time(b) * 1e3 / ncopy
+        del buf
+        torch.cuda.empty_cache()
+        rows.append({"keys_per_launch": banks * n, "algorithmic_bytes": alg, "score_us": score_us,
+                     "copy_us": copy_us, "score_gbps": alg / score_us / 1e3, "copy_gbps": 2 * half / copy_us / 1e3})
+
+    def fit(key):
+        x = np.array([r["algorithmic_bytes"] for r in rows], np.float64)
+        y = np.array([r[key] for r in rows], np.float64)
+        slope, t0 = np.polyfit(x, y, 1)
+        bw = 1.0 / slope / 1e3  # bytes per microsecond -> GB/s
+        return {"t0_us": float(t0), "bw_inf_gbps": float(bw), "bw_inf_frac_of_8tbs": float(bw / HBM_PEAK_GBPS),
+                "max_rel_residual": float(np.max(np.abs(y - (t0 + slope * x)) / y))}
+
+    return {"workload": "decode8b shapes, 64 banks x n keys, G=4, b=3 (72 algorithmic bytes per key); "
+                        "random bank bytes, distinct buffers cycled",
+            "rows": rows, "fit_score": fit("score_us"), "fit_copy": fit("copy_us")}
+
+
 def attend_extra(tq, device, layers=4, reps=12):
     """Decode attention over decode8b layers (64 banks x 32768 tokens, G = 4): keys at b=4
     (3-bit codebook + sketch), values MSE-only at 3 bits; `layers` distinct layers cycled so
@@ -582,7 +696,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device copy of this many MiB (calibrates the HBM traffic counters)")
-    ap.add_argument("--only", choices=["attend", "longctx", "search", "append", "variants", "small", "halfnorm"],
+    ap.add_argument("--only", choices=["attend", "longctx", "search", "append", "variants", "small", "halfnorm",
+                                       "sweep", "fp32"],
                     help="run one extra section alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -599,7 +714,8 @@ def main():
     torch.cuda.set_device(0)
     if args.only:
         fn = {"attend": attend_extra, "longctx": longctx_extra, "search": search_extra, "append": append_extra,
-              "variants": variants_extra, "small": small_extra,
+              "variants": variants_extra, "small": small_extra, "sweep": launch_sweep,
+              "fp32": lambda t, d: fp32_comparator(t, d, args.layers, max(args.steps // 4, 1), float("nan")),
               "halfnorm": lambda t, d: halfnorm_extra(t, d, args.layers, args.steps, float("nan"))}[args.only]
         print(json.dumps({args.only: fn(tq, device)}))
         return
@@ -640,7 +756,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "i8-limb exact (i32 acc, f64 combine)",
         "data": "synthetic",
         "config": {
             "workload": "decode8b: 32 layers x batch 8 x 8 kv heads x 32768 keys, G=4 queries per kv head, "
@@ -691,25 +807,10 @@ def main():
         torch.cuda.empty_cache()
 
         log("fp32 unquantized-keys comparator")
-        nfp = 4  # distinct fp32 layers (4.3 GB, far beyond the 256 MB last-level cache), cycled
-        kf = [workloads.keys_device(cfg, l, device, dtype=torch.float32) for l in range(nfp)]
-        qf = [workloads.queries_device(cfg, l, device) for l in range(nfp)]
-        sf = torch.empty((cfg.banks, cfg.G, cfg.tokens), dtype=torch.float32, device=device)
-
-        def fp32_step():
-            for layer in range(L):
-                tq.tq_fp32_logits(kf[layer % nfp], qf[layer % nfp], sf)
-
-        wallf, kernf = timed(fp32_step, max(args.steps // 4, 1), 1, L)
-        fbytes = cfg.banks * cfg.tokens * (4 * cfg.d + 4 * cfg.G)
-        out["fp32_comparator"] = {
-            "value": pairs_per_step / (wallf / max(args.steps // 4, 1)),
-            "unit": "pairs/s",
-            "kernel_gbps": fbytes / (np.mean(kernf) * 1e-3) / 1e9,
-            "speedup_of_packed_b3": (np.mean(kernf)) / kavg,
-            "context": "the pages quote up to 8x for 4-bit keys vs 32-bit keys on H100",
-        }
-        del kf
+        out["fp32_comparator"] = fp32_comparator(tq, device, L, max(args.steps // 4, 1), kavg)
+        torch.cuda.empty_cache()
+        log("launch-size sweep")
+        out["launch_sweep"] = launch_sweep(tq, device)
         torch.cuda.empty_cache()
 
         log("long-context mixed bit widths")
