@@ -19,18 +19,32 @@
 
 namespace tq {
 
-// Each operand fragment read from LDS feeds the MFMAs of LDS_TB key tiles: with one tile per
-// read the LDS bandwidth (128 B/clk per CU) bounds the kernel at half the int8 MFMA rate. Two
-// tiles in flight take 256 VGPRs, so a work-group has 8 waves (two per SIMD).
+// Each operand fragment read from LDS (1 KiB per wave) feeds the MFMAs of lds_tb() key tiles,
+// and each expanded key operand the MFMAs of lds_rows() row tiles. Per MFMA the CU's LDS
+// (128 B/clk) and vector ALU (4 ops per 16-cycle MFMA per SIMD) are then loaded with 1 KiB /
+// TB and 4 / RQ. A work-group has 8 waves (two per SIMD, 256 VGPRs each): with two tiles per
+// read the key words are double-buffered in registers; with four they are loaded once per
+// batch and the SIMD's other wave computes while they arrive.
 constexpr int LDS_WAVES = 8;
-constexpr int LDS_TB = 2;
 
-// row tiles of operands a work-group holds in LDS (fragments and constants in ~150 KiB)
+template <class L>
+constexpr int lds_tb() {
+    return L::NF * 1024 > 50 * 1024 ? 4 : 2;
+}
+// double-buffered key loads (two batches in registers) for two tiles per read
+template <class L>
+constexpr bool lds_db() {
+    return lds_tb<L>() <= 2;
+}
+
+// row tiles of operands a work-group holds in LDS (fragments and constants in ~150 KiB); at
+// most two beside four key tiles per read (their accumulators share the register budget)
 template <class L>
 constexpr int lds_rows() {
     constexpr int per = L::NF * 1024 + 4 * L::NCLS * 16;
     constexpr int r = (150 * 1024) / per;
-    return r > 4 ? 4 : (r < 1 ? 1 : r);
+    constexpr int cap = lds_tb<L>() > 2 ? 2 : 4;
+    return r > cap ? cap : (r < 1 ? 1 : r);
 }
 
 template <class L>
@@ -55,19 +69,34 @@ __device__ __forceinline__ void topk_insert(float &lv, int &li, float v, int id,
     }
 }
 
-// Offers the 16 estimates of lane group g (key index key, valid flag ok) to query list
-// (lv, li): those that beat the current k-th entry are inserted in lane order.
-__device__ __forceinline__ void topk_offer(float &lv, int &li, float est, int key, bool ok, int g, int gl, int k,
-                                           int lane) {
-    const float tv = __shfl(lv, k - 1, 64);
-    const int ti = __shfl(li, k - 1, 64);
-    uint64_t m = __ballot(ok && gl == g && topk_better(est, key, tv, ti));
+// Offers a tile's estimates to the four lists of a row tile: lane group g holds the 16
+// estimates (est, key index key, valid flag ok) of query g, whose list is (lv[g], li[g]) and
+// whose current k-th entry every lane of group g keeps in (tv, ti). One compare and one ballot
+// find the candidates of all four queries; those (rare once the lists fill) are inserted in
+// lane order, and the thresholds are then refreshed. A stale threshold only admits more
+// candidates, and inserting one that no longer qualifies leaves the list unchanged.
+__device__ __forceinline__ void topk_offer4(float (&lv)[4], int (&li)[4], float &tv, int &ti, float est, int key,
+                                            bool ok, int gl, int k, int lane) {
+    uint64_t m = __ballot(ok && topk_better(est, key, tv, ti));
+    if (!m) return;
     while (m) {
         const int src = __builtin_ctzll(m);
         m &= m - 1;
         const float v = __shfl(est, src, 64);
         const int id = __shfl(key, src, 64);
-        topk_insert(lv, li, v, id, lane);
+        const int g = src >> 4;  // wave-uniform
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q == g) topk_insert(lv[q], li[q], v, id, lane);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float t = __shfl(lv[q], k - 1, 64);
+        const int i = __shfl(li[q], k - 1, 64);
+        if (gl == q) {
+            tv = t;
+            ti = i;
+        }
     }
 }
 
@@ -120,25 +149,38 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
     const int per = (c1 - c0 + LDS_WAVES - 1) / LDS_WAVES;
     const int t0 = min(c0 + wv * per, c1), t1 = min(t0 + per, c1);
     const long n_pad = (long)n_tiles * 16;
-    constexpr int TB = LDS_TB;
+    constexpr int TB = lds_tb<L>();
+    constexpr bool DB = lds_db<L>();
     TileStream<L, 1, TB> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
                            rnorms + (size_t)bank * n_pad, nullptr, n, G, t0, t1};
     ts.init_lane();
     float *ob = TOPK ? nullptr : scores + (size_t)bank * G * n;
 
-    // per-query top-k lists (4 queries per row tile), entry i in lane i
-    float lv[TOPK ? RQ * 4 : 1];
-    int li[TOPK ? RQ * 4 : 1];
+    // per-query top-k lists (4 queries per row tile), entry i in lane i, and the k-th entry of
+    // the lane's own query in each row tile
+    float lv[RQ][4];
+    int li[RQ][4];
+    float tv[RQ];
+    int ti[RQ];
 #pragma unroll
-    for (int e = 0; e < (TOPK ? RQ * 4 : 1); ++e) {
-        lv[e] = -INFINITY;
-        li[e] = INT32_MAX;
+    for (int rt = 0; rt < RQ; ++rt) {
+        tv[rt] = -INFINITY;
+        ti[rt] = INT32_MAX;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            lv[rt][g] = -INFINITY;
+            li[rt][g] = INT32_MAX;
+        }
     }
 
     TileBatch<L, TB> A, B;
-    if (t0 < t1) ts.load(A, t0);
+    if (DB && t0 < t1) ts.load(A, t0);
     for (int t = t0; t < t1; t += TB) {
-        if (t + TB < t1) ts.load(B, t + TB);
+        if constexpr (DB) {
+            if (t + TB < t1) ts.load(B, t + TB);
+        } else {
+            ts.load(A, t);
+        }
         i32x4 acc[TB][RQ][L::NCLS];
 #pragma unroll
         for (int u = 0; u < TB; ++u)
@@ -197,15 +239,13 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
             const int gq = 4 * (rt0 + rt) + gl;
             if constexpr (TOPK) {
                 // queries past G never enter a list (their lists are not written back)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    topk_offer(lv[4 * rt + g], li[4 * rt + g], e, (int)key, key_live && gq < G, g, gl, k, lane);
+                topk_offer4(lv[rt], li[rt], tv[rt], ti[rt], e, (int)key, key_live && gq < G, gl, k, lane);
             } else {
                 if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
             }
         }
         }
-        A = B;
+        if constexpr (DB) A = B;
     }
     if constexpr (TOPK) {
         // partial lists: [bank][query][chunk * LDS_WAVES + wave][k]
@@ -217,8 +257,8 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
                 const int gq = 4 * (rt0 + rt) + g;
                 if (gq < G && lane < k) {
                     const size_t o = (((size_t)bank * G + gq) * slots + slot) * k + lane;
-                    part_v[o] = lv[4 * rt + g];
-                    part_i[o] = li[4 * rt + g];
+                    part_v[o] = lv[rt][g];
+                    part_i[o] = li[rt][g];
                 }
             }
     }
