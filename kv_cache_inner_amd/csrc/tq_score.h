@@ -673,10 +673,14 @@ constexpr int RING_WAVES = 16;
 
 template <class L>
 constexpr int ring_slots() {
-    // the ring and the prologue's scratch within 160 KiB of LDS; at most 8 tiles ahead
+    // the ring and the prologue's scratch within 160 KiB of LDS; at most 8 tiles ahead, 6 for
+    // two channel groups (whose three estimator terms leave no registers for a deeper
+    // unrolled ring: with 8 slots one VGPR spilled to scratch, and the launch was about 2 %
+    // slower on the long-context banks)
     constexpr int budget = 160 * 1024 - (int)sizeof(FusedLds<L, 1>);
     constexpr int s = budget / (RING_WAVES * RingTile<L>::WORDS * 4);
-    return (s > 8 ? 8 : s) & ~1;  // even: the steady state fills the ring by halves
+    constexpr int cap = L::NG > 1 ? 6 : 8;
+    return (s > cap ? cap : s) & ~1;  // even: the steady state fills the ring by halves
 }
 
 // Norms per 16-byte lane load (4 float32 or 8 binary16), and the lanes that load a tile's
