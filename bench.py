@@ -249,26 +249,36 @@ def cpu_baseline(cfg, bits, banks, layers):
     }
 
 
-def copy_ceiling(tq, device, nbytes, copies=4, reps=12):
+def copy_ceiling(tq, device, nbytes, reps=32):
     """Plain device copy moving the same total bytes as one score launch (half read, half
-    written), cycled over `copies` distinct buffer pairs so that no launch is served from
-    the 256 MB last-level cache: the HBM rate a streaming kernel of this size can reach on
-    this device."""
+    written), cycled over distinct buffer pairs (about 1.2 GB in all, so that no launch is
+    served from the 256 MB last-level cache) and launched back to back with pre-marshalled
+    arguments, as the scorer's launches are: the HBM rate a streaming kernel of this size
+    reaches on this device, launch overhead included."""
+    import ctypes
+
     import torch
 
     half = (nbytes // 2 + 15) // 16 * 16
-    src = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(copies)]
-    dst = [torch.empty(half, dtype=torch.uint8, device=device) for _ in range(copies)]
-    for i in range(copies):
-        tq.tq_copy(src[i], dst[i])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for r, (a, b) in enumerate(ev):
-        a.record()
-        tq.tq_copy(src[r % copies], dst[r % copies])
-        b.record()
+    copies = max(2, -(-int(1.2e9) // (2 * half)))
+    buf = torch.empty((copies, 2, half), dtype=torch.uint8, device=device)
+    lib = tq._lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = [(buf[i % copies, 0].data_ptr(), buf[i % copies, 1].data_ptr(), half, stream)
+             for i in range(max(reps, copies))]
+    for c in calls[:copies]:
+        if lib.tq_copy(*c):
+            raise RuntimeError("tq_copy failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for c in calls:
+        lib.tq_copy(*c)
+    b.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    return {"bytes": 2 * half, "ms": ms, "gbps": 2 * half / (ms * 1e-3) / 1e9}
+    ms = a.elapsed_time(b) / len(calls)
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * half, "ms": ms, "gbps": 2 * half / (ms * 1e-3) / 1e9, "copies_cycled": copies}
 
 
 def longctx_extra(tq, device):
@@ -502,20 +512,9 @@ def launch_sweep(tq, device, reps=32):
         torch.cuda.synchronize()
         score_us = a.elapsed_time(b) * 1e3 / len(calls)
         del bits, norms, rnorms, scores, structs, calls
-        half = (alg // 2 + 15) // 16 * 16
-        cc = max(2, -(-int(1.2e9) // (2 * half)))
-        buf = torch.empty((cc, 2, half), dtype=torch.uint8, device=device)
-        for i in range(cc):
-            tq.tq_copy(buf[i, 0], buf[i, 1])
-        a.record()
-        ncopy = max(reps, cc)
-        for i in range(ncopy):
-            tq.tq_copy(buf[i % cc, 0], buf[i % cc, 1])
-        b.record()
-        torch.cuda.synchronize()
-        copy_us = a.elapsed_time(b) * 1e3 / ncopy
-        del buf
-        torch.cuda.empty_cache()
+        cp = copy_ceiling(tq, device, alg, reps)
+        half = cp["bytes"] // 2
+        copy_us = cp["ms"] * 1e3
         rows.append({"keys_per_launch": banks * n, "algorithmic_bytes": alg, "score_us": score_us,
                      "copy_us": copy_us, "score_gbps": alg / score_us / 1e3, "copy_gbps": 2 * half / copy_us / 1e3})
 
