@@ -13,6 +13,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resources (raw, untyped access): the fourth descriptor dword, whose data-format
+// field must be non-zero (32-bit) on gfx9 parts. Accesses past the byte range are dropped.
+constexpr int BUF_DWORD3 = 0x00020000;
+// cache-policy bits of a memory instruction on gfx950: sc0, nt, sc1
+constexpr int CPOL_SC0 = 1, CPOL_NT = 2, CPOL_SC1 = 16;
+
 // Compile-time loop: calls f(std::integral_constant<int, I>) for I = 0..N-1.
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {

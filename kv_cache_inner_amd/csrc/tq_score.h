@@ -904,16 +904,30 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
     const int full = (int)(n >> 4);  // tiles whose 16 keys are all below n
     const int loff = gl * (int)n + j;  // lane offset into the bank's score rows
     // Scores stored one float per lane (16 lanes: 64 contiguous bytes of a query row) carry the
-    // non-temporal hint: measured against plain stores in one process on one box, the
-    // long-context banks (two groups, whose ring halves hold 3 tiles) scored about 8 % faster
-    // and the decode shapes, whose last tiles take this path, about 1 % faster. The 16-byte
-    // stores below stay plain: with the hint the decode shapes were about 3 % slower.
+    // non-temporal hint in the per-tile loop at the end of a run, and in the steady state only
+    // for two channel groups. Measured against plain stores in one process on one box: hint
+    // everywhere made the long-context banks (two groups, 3-tile ring halves) about 8 % faster
+    // but the decode shapes at b = 4 (one group, 3-tile halves) about 8 % slower; the hint in
+    // the end loop alone left b = 4 unchanged, made b = 3 (whose last 8 tiles per wave take
+    // that loop) about 2 % faster and gave the long-context banks under half of their gain.
+    constexpr bool NT_GROUP = L::NG > 1;
+    auto store1 = [](float *p, float v) {
+        if constexpr (NT_GROUP)
+            __builtin_nontemporal_store(v, p);
+        else
+            *p = v;
+    };
     // Scores of a group of four tiles leave as one 16-byte store per lane: a 4 x 4 transpose
     // inside each lane quad (tile index <-> key bits 0-1) gives lane 4c + x the keys
     // 4c .. 4c + 3 of tile x, so a query row's 16 lanes cover 256 contiguous bytes with one
-    // instruction. Rows must start 16-byte aligned (n a multiple of 4).
-    const bool wide = U == 4 && (n & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+    // instruction. Rows must start 16-byte aligned (n a multiple of 4). These stores go
+    // through a buffer resource over the bank's score rows (a 32-bit byte range: n < 2^27 at
+    // G = 4) with system scope (sc0 sc1: written through the L2): in three same-process A/Bs
+    // the decode shapes were 0.9-1.5 % faster than with plain stores (and about 3 % slower
+    // with the non-temporal hint instead).
+    const bool wide = U == 4 && (n & 3) == 0 && ((uintptr_t)scores & 15) == 0 && n < (1L << 27);
     const int wide_off = gl * (int)n + 16 * (lane & 3) + 4 * ((lane >> 2) & 3);
+    const __amdgpu_buffer_rsrc_t srows = __builtin_amdgcn_make_buffer_rsrc(ob, 0, wide ? (int)(16 * n) : 0, BUF_DWORD3);
     auto store_group = [&](float *base, const float(&pv)[U]) {
         if constexpr (U == 4) {
             float v0 = pv[0], v1 = pv[1], v2 = pv[2], v3 = pv[3];
@@ -930,7 +944,10 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
             r = dpp_mov_f32<DPP_XOR2>(h ? v1 : v3);
             v1 = h ? r : v1;
             v3 = h ? v3 : r;
-            *reinterpret_cast<f32x4 *>(base + wide_off) = f32x4{v0, v1, v2, v3};
+            const uint32_t off = 4u * (uint32_t)((base - ob) + wide_off);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2),
+                                                         __float_as_uint(v3)},
+                                                   srows, off, 0, CPOL_SC0 | CPOL_SC1);
         }
     };
     if (G == 4 && 2 * S <= nt && t0 + U <= full) {
@@ -949,7 +966,7 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
                     if (wide) {
                         if (k == 0) store_group(prev_out, pend);
                     } else {
-                        __builtin_nontemporal_store(pend[k], prev_out + loff + 16 * k);
+                        store1(prev_out + loff + 16 * k, pend[k]);
                     }
                 }
                 const int tn = t0 + i + S + k;
@@ -966,7 +983,7 @@ __global__ __launch_bounds__(RING_WAVES * 64) void score_ring_kernel(
         } else {
             static_for<U>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
-                __builtin_nontemporal_store(pend[k], last_out + loff + 16 * k);
+                store1(last_out + loff + 16 * k, pend[k]);
             });
         }
     }
