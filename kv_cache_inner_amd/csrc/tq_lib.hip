@@ -394,6 +394,10 @@ static LdsPlan lds_plan(int64_t banks, int64_t n, int Gpad) {
     if (max_kc < 1) max_kc = 1;
     if (kc > max_kc) kc = max_kc;
     if (kc < 1) kc = 1;
+    // a chunk's bit words within a 32-bit byte range (the streamed kernel reads them through
+    // one buffer resource per work-group)
+    const int64_t min_kc = (n_tiles * L::W * 64 + INT32_MAX - 1) / INT32_MAX;
+    if (kc < min_kc) kc = min_kc;
     pl.chunk_tiles = (int)((n_tiles + kc - 1) / kc);
     pl.kchunks = (int)((n_tiles + pl.chunk_tiles - 1) / pl.chunk_tiles);
     pl.grid = banks * pl.kchunks * pl.qblocks;

@@ -52,6 +52,59 @@ constexpr bool lds_fits() {
     return L::NF * 1024 + 4 * L::NCLS * 16 <= 150 * 1024;
 }
 
+// Streamed batches (four key tiles per operand read). A batch's 2 NQ MFMA steps (derived
+// quad, half) run in a fixed order that takes the derived words word-group by word-group
+// (every Walsh subset of stored words 4k..4k+3 of a class, then the next four words, the
+// sketch words last), so each stored quad is read by steps close together. Its loads are
+// issued LDS_LA quads before its first step (those of the next batch's first quads during
+// this batch's last ones): the key words in registers are then those of a few quads, not
+// of the whole batch, and no batch waits for a round trip to memory at its start. The freed
+// registers hold the next step's expanded key operand and operand fragments, formed while
+// the current step's MFMAs run (one MFMA, then two of the next step's vector instructions).
+constexpr int LDS_LA = 8;
+
+template <class L>
+struct StreamOrder {
+    struct Table {
+        int v[64];
+    };
+    static_assert(L::NQ <= 64 && L::NSQ <= 64, "stream tables");
+    // sort key of derived quad q: class, then word index inside its plane, then subset
+    static constexpr int key(int q) {
+        for (int g = 0; g < 4; ++g) {
+            const DWord w = L::dword(4 * q + g);
+            if (w.cls >= 0) return ((w.cls * 4096) + (w.k - g)) * 8 + w.sub;
+        }
+        return 1 << 30;  // padding only: last
+    }
+    static constexpr Table make_order() {
+        Table keys{}, ord{};
+        for (int q = 0; q < L::NQ; ++q) keys.v[q] = key(q);
+        for (int q = 0; q < L::NQ; ++q) {
+            int rank = 0;
+            for (int p = 0; p < L::NQ; ++p)
+                if (keys.v[p] < keys.v[q] || (keys.v[p] == keys.v[q] && p < q)) ++rank;
+            ord.v[rank] = q;
+        }
+        return ord;
+    }
+    static constexpr Table order = make_order();
+    static constexpr Table make_first() {
+        Table f{};
+        for (int sq = 0; sq < L::NSQ; ++sq) f.v[sq] = L::NQ;
+        for (int i = L::NQ - 1; i >= 0; --i) {
+            const int q = order.v[i];
+            for (int c = 0; c < L::quad_nx(q); ++c) f.v[L::quad_sq(q, c)] = i;
+        }
+        return f;
+    }
+    static constexpr Table first = make_first();
+    // the i-th derived quad of a batch
+    static constexpr int at(int i) { return order.v[i]; }
+    // position of the first quad that reads stored quad sq (NQ: none)
+    static constexpr int first_use(int sq) { return first.v[sq]; }
+};
+
 // Entry i of a per-query list sits in lane i. `better` orders candidates: larger value
 // first, equal values by lower index.
 __device__ __forceinline__ bool topk_better(float v, int i, float lv, int li) { return v > lv || (v == lv && i < li); }
@@ -173,14 +226,39 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
         }
     }
 
-    TileBatch<L, TB> A, B;
-    if (DB && t0 < t1) ts.load(A, t0);
-    for (int t = t0; t < t1; t += TB) {
-        if constexpr (DB) {
-            if (t + TB < t1) ts.load(B, t + TB);
-        } else {
-            ts.load(A, t);
+    // estimates of the batch at tile t from its accumulators: stored, or offered to the lists
+    auto finish = [&](int t, const float (&nu)[TB][L::NG], const float (&rho)[TB], i32x4 (&acc)[TB][RQ][L::NCLS]) {
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            if (t + u >= t1) break;
+            const long key = (long)(t + u) * 16 + j;
+            const bool key_live = key < n;
+#pragma unroll
+            for (int rt = 0; rt < RQ; ++rt) {
+                double est = 0.0;
+                static_for<L::NCLS>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    constexpr int g = c < L::NG ? c : 0;
+                    const double s = c < L::NG ? (double)nu[u][g] : (double)rho[u];
+                    est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[u][rt][c]), cs[rt][c], ck[rt][c]), est);
+                });
+                const float e = (float)est;
+                const int gq = 4 * (rt0 + rt) + gl;
+                if constexpr (TOPK) {
+                    // queries past G never enter a list (their lists are not written back)
+                    topk_offer4(lv[rt], li[rt], tv[rt], ti[rt], e, (int)key, key_live && gq < G, gl, k, lane);
+                } else {
+                    if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
+                }
+            }
         }
+    };
+
+    if constexpr (DB) {
+    TileBatch<L, TB> A, B;
+    if (t0 < t1) ts.load(A, t0);
+    for (int t = t0; t < t1; t += TB) {
+        if (t + TB < t1) ts.load(B, t + TB);
         i32x4 acc[TB][RQ][L::NCLS];
 #pragma unroll
         for (int u = 0; u < TB; ++u)
@@ -221,31 +299,149 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
             // once would exceed the register budget)
             asm volatile("" ::: "memory");
         });
+        finish(t, A.nu, A.rho, acc);
+        A = B;
+    }
+    } else {
+    // streamed batches: stored quad sq of tile u in kw[sq][u] (the next batch's first quads
+    // in kn until the batch ends)
+    using SO = StreamOrder<L>;
+    constexpr int NSTEP = 2 * L::NQ;
+    const uint32_t *bbank = bits + (size_t)bank * n_tiles * L::W * 16;
+    const typename L::NormT *nbank = norms + (size_t)bank * n_pad * L::NG;
+    const typename L::NormT *rbank = rnorms + (size_t)bank * n_pad;
+    // The chunk's bit words through one buffer resource (the host keeps a chunk below 2 GiB):
+    // a load is then a scalar offset (tile, stored quad) plus this lane's 32-bit offset, with
+    // no per-load address arithmetic on the vector ALU. Word 4 sq + gl of key j of a tile
+    // sits 4 (16 (4 sq + gl) + j) bytes into it.
+    const __amdgpu_buffer_rsrc_t chunk_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(bbank) + (size_t)c0 * (L::W * 16), 0, (c1 - c0) * (L::W * 64), BUF_DWORD3);
+    const int lane_off = 4 * (16 * gl + j);
+    auto load_sq = [&](uint32_t (&dst)[TB], int sq, int tile0) {
+        const bool live = 4 * sq + gl < L::W;
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-        if (t + u >= t1) break;
-        const long key = (long)(t + u) * 16 + j;
-        const bool key_live = key < n;
+            const int tile = min(tile0 + u, t1 - 1);  // clamped: the last batch may be partial
+            const int soff = (tile - c0) * (L::W * 64) + 256 * sq;
+            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(chunk_rs, live ? lane_off : 4 * j, soff, 0);
+            dst[u] = live ? v : 0u;
+        }
+    };
+    uint32_t kw[L::NSQ][TB];
+    static_for<L::NSQ>([&](auto sc) {
+        constexpr int sq = decltype(sc)::value;
+        if constexpr (SO::first_use(sq) < LDS_LA)
+            if (t0 < t1) load_sq(kw[sq], sq, t0);
+    });
+    for (int t = t0; t < t1; t += TB) {
+        float nu[TB][L::NG], rho[TB];
 #pragma unroll
-        for (int rt = 0; rt < RQ; ++rt) {
-            double est = 0.0;
+        for (int u = 0; u < TB; ++u) {
+            const int tile = min(t + u, t1 - 1);
+#pragma unroll
+            for (int g = 0; g < L::NG; ++g) nu[u][g] = norm_f32(nbank[(size_t)tile * (16 * L::NG) + j * L::NG + g]);
+            rho[u] = norm_f32(rbank[(size_t)tile * 16 + j]);
+        }
+        uint32_t kn[L::NSQ][TB];
+        i32x4 acc[TB][RQ][L::NCLS];
+#pragma unroll
+        for (int u = 0; u < TB; ++u)
+#pragma unroll
+            for (int rt = 0; rt < RQ; ++rt)
+#pragma unroll
+                for (int c = 0; c < L::NCLS; ++c) acc[u][rt][c] = i32x4{0, 0, 0, 0};
+        // operands of step s = (position i, half h): expanded key words and fragments
+        auto der_of = [&](auto ic, uint32_t (&der)[TB]) {
+            constexpr int q = SO::at(decltype(ic)::value);
+            constexpr int nx = L::quad_nx(q);
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                der[u] = kw[L::quad_sq(q, 0)][u];
+                if constexpr (nx > 1) der[u] ^= kw[L::quad_sq(q, 1)][u];
+                if constexpr (nx > 2) der[u] ^= kw[L::quad_sq(q, 2)][u];
+            }
+        };
+        auto frags_of = [&](auto sc, i8x16 (&a)[L::NCLS][RQ]) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int q = SO::at(s / 2), h = s % 2;
             static_for<L::NCLS>([&](auto cc) {
                 constexpr int c = decltype(cc)::value;
-                constexpr int g = c < L::NG ? c : 0;
-                const double s = c < L::NG ? (double)A.nu[u][g] : (double)A.rho[u];
-                est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(acc[u][rt][c]), cs[rt][c], ck[rt][c]), est);
+                if constexpr (L::quad_has(q, c)) {
+#pragma unroll
+                    for (int rt = 0; rt < RQ; ++rt)
+                        a[c][rt] = *reinterpret_cast<const i8x16 *>(&fa[rt][L::frag_index(q, h, c)][lane][0]);
+                }
             });
-            const float e = (float)est;
-            const int gq = 4 * (rt0 + rt) + gl;
-            if constexpr (TOPK) {
-                // queries past G never enter a list (their lists are not written back)
-                topk_offer4(lv[rt], li[rt], tv[rt], ti[rt], e, (int)key, key_live && gq < G, gl, k, lane);
-            } else {
-                if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
+        };
+        uint32_t der[TB];
+        i8x16 bk[TB], ak[L::NCLS][RQ];
+        der_of(std::integral_constant<int, 0>{}, der);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) bk[u] = expand_half<0>(der[u]);
+        frags_of(std::integral_constant<int, 0>{}, ak);
+        static_for<NSTEP>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int i = s / 2, h = s % 2;
+            constexpr int q = SO::at(i);
+            __builtin_amdgcn_sched_barrier(0);
+            // loads of the stored quads first read LDS_LA quads ahead (this batch or the next)
+            if constexpr (h == 0) {
+                static_for<L::NSQ>([&](auto qc) {
+                    constexpr int sq = decltype(qc)::value;
+                    constexpr int fu = SO::first_use(sq);
+                    if constexpr (fu < L::NQ && fu == i + LDS_LA) load_sq(kw[sq], sq, t);
+                    if constexpr (fu < LDS_LA && fu == i + LDS_LA - L::NQ) load_sq(kn[sq], sq, t + TB);
+                });
             }
-        }
-        }
-        if constexpr (DB) A = B;
+            // the next step's operands, formed while this step's MFMAs run
+            i8x16 bn[TB], an[L::NCLS][RQ];
+            if constexpr (s + 1 < NSTEP) {
+                if constexpr (h == 1) der_of(std::integral_constant<int, i + 1>{}, der);
+#pragma unroll
+                for (int u = 0; u < TB; ++u) bn[u] = expand_half<(s + 1) % 2>(der[u]);
+                frags_of(std::integral_constant<int, s + 1>{}, an);
+            }
+            constexpr int nmf = [] {
+                int m = 0;
+                for (int c = 0; c < L::NCLS; ++c) m += L::quad_has(q, c) ? RQ * TB : 0;
+                return m;
+            }();
+            static_for<L::NCLS>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if constexpr (L::quad_has(q, c)) {
+#pragma unroll
+                    for (int rt = 0; rt < RQ; ++rt)
+#pragma unroll
+                        for (int u = 0; u < TB; ++u)
+                            acc[u][rt][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ak[c][rt], bk[u], acc[u][rt][c], 0, 0, 0);
+                }
+            });
+            // schedule: the fragment reads, then each MFMA followed by two vector instructions
+            __builtin_amdgcn_sched_group_barrier(0x100, RQ, 0);
+            static_for<nmf>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            });
+            if constexpr (s + 1 < NSTEP) {
+#pragma unroll
+                for (int u = 0; u < TB; ++u) bk[u] = bn[u];
+                static_for<L::NCLS>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+#pragma unroll
+                    for (int rt = 0; rt < RQ; ++rt) ak[c][rt] = an[c][rt];
+                });
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        finish(t, nu, rho, acc);
+        static_for<L::NSQ>([&](auto sc) {
+            constexpr int sq = decltype(sc)::value;
+            if constexpr (SO::first_use(sq) < LDS_LA) {
+#pragma unroll
+                for (int u = 0; u < TB; ++u) kw[sq][u] = kn[sq][u];
+            }
+        });
+    }
     }
     if constexpr (TOPK) {
         // partial lists: [bank][query][chunk * LDS_WAVES + wave][k]
