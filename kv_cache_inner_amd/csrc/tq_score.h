@@ -121,7 +121,9 @@ template <class L, int RT, int NT>
 struct PrepRegs {
     static constexpr int ITEMS = PrepItem<L, RT>::NR * RT * PrepItem<L, RT>::CPR;
     static constexpr int PER = (ITEMS + NT - 1) / NT;  // items per thread
-    static constexpr int PRE = PER < 2 ? PER : 2;      // of which preloaded (register budget)
+    // of which preloaded: two where a thread has 256 VGPRs, one in 1024-thread work-groups
+    // (128 VGPRs; two 32-column chunks there spilled to scratch at d = 256)
+    static constexpr int PRE = PER < 2 ? PER : (NT >= 1024 ? 1 : 2);
     float qv, qg;
     f32x4 m[PRE][PrepItem<L, RT>::CH / 4];
 };

@@ -108,15 +108,19 @@ def test_score_ragged_shapes(tq, n, G):
     _score_check(tq, cfg, 3, keys, q)
 
 
+@pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("d", [64, 256])
-def test_score_other_head_dims(tq, d):
+def test_score_other_head_dims(tq, d, bits):
+    """d = 64 and 256 at G = 4 and G = 1 (the fused scorer with operands in registers;
+    1024-thread work-groups at G = 1)."""
     import dataclasses
 
     cfg = dataclasses.replace(workloads.CONFIGS["decode8b"], d=d, m=d, cfg_id=40 + d // 64)
-    say(f"score d={d}")
     keys = workloads.keys(cfg, n=300, banks=[0])
-    q = workloads.queries(cfg, banks=[0], G=4)
-    _score_check(tq, cfg, 3, keys, q)
+    for G in (4, 1):
+        say(f"score d={d} b={bits} G={G}")
+        q = workloads.queries(cfg, banks=[0], G=G)
+        _score_check(tq, cfg, bits, keys, q)
 
 
 def test_score_random_banks_full_decode8b_layer(tq):
