@@ -37,17 +37,6 @@ __device__ __forceinline__ float norm_f32(float v) { return v; }
 __device__ __forceinline__ float norm_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f32_to_binary16(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-// A wave-uniform pointer held in scalar registers: memory accesses through it take the
-// scalar-base form (base in SGPRs, 32-bit per-lane offset) instead of 64-bit vector address
-// arithmetic per access.
-template <class T>
-__device__ __forceinline__ const T *uniform_ptr(const T *p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const T *>((uintptr_t)(((uint64_t)hi << 32) | lo));
-}
-
 // Work-group barrier over LDS traffic only: it waits for this wave's LDS operations but not
 // for its vector-memory loads, so loads issued earlier (direct-to-LDS or into registers)
 // stay in flight (a __syncthreads() would drain them all). Only for code whose cross-wave
