@@ -306,6 +306,8 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
     // streamed batches: stored quad sq of tile u in kw[sq][u] (the next batch's first quads
     // in kn until the batch ends)
     using SO = StreamOrder<L>;
+    // every stored quad is loaded in a batch's positions 0 .. NQ - 1 for this batch or the next
+    static_assert(L::NQ >= LDS_LA, "the lookahead spans at most one batch");
     constexpr int NSTEP = 2 * L::NQ;
     const uint32_t *bbank = bits + (size_t)bank * n_tiles * L::W * 16;
     const typename L::NormT *nbank = norms + (size_t)bank * n_pad * L::NG;
