@@ -56,7 +56,8 @@ def test_encode_search_small(tq, bits):
     say("   report", rep)
 
 
-@pytest.mark.parametrize("bits,n,G,k", [(4, 5003, 37, 10), (2, 3001, 9, 10), (4, 700, 5, 64), (2, 900, 3, 1)])
+@pytest.mark.parametrize("bits,n,G,k", [(4, 5003, 37, 10), (2, 3001, 9, 10), (4, 700, 5, 64), (2, 900, 3, 1),
+                                        (4, 33, 5, 10), (2, 40, 6, 7)])
 def test_topk_search_small(tq, bits, n, G, k):
     import torch
 
@@ -104,10 +105,11 @@ def test_topk_ties_by_lower_index(tq):
     assert first == [5] + list(range(300, 310)), first
 
 
-@pytest.mark.parametrize("cfg_name,bits,n,G", [("decode3b", 3, 777, 40), ("search", 4, 1500, 4), ("search", 2, 333, 21)])
+@pytest.mark.parametrize("cfg_name,bits,n,G", [("decode3b", 3, 777, 40), ("search", 4, 1500, 4), ("search", 2, 333, 21),
+                                              ("search", 4, 1, 4), ("search", 4, 17, 6)])
 def test_score_large_operands(tq, cfg_name, bits, n, G):
     """tq_score where the operands go through LDS: more than 16 queries per bank, or
-    768-dimensional keys."""
+    768-dimensional keys (down to one key: most waves get no tile, the one batch is partial)."""
     import torch
 
     cfg = workloads.CONFIGS[cfg_name]
