@@ -228,8 +228,9 @@ int tq_score(const tq_params *p, const tq_bank *in, int64_t banks, int64_t n, co
  * by lower key index; the estimates are those tq_score returns (fp32), ranked as
  * fp32. vals (device) float32 [banks][G][k], idx (device) int32 [banks][G][k].
  * q (device) float32 [banks][G][d], any G >= 1. 1 <= k <= 64 and k <= n, else
- * TQ_ERR_ARG; n > INT32_MAX (indices past the int32 range): TQ_ERR_UNSUPPORTED. The score rows are never written to memory: the prepared query
- * operands and the per-wave partial top-k lists live in `workspace` (device) of
+ * TQ_ERR_ARG; n > INT32_MAX (indices past the int32 range): TQ_ERR_UNSUPPORTED.
+ * The score rows are never written to memory: the prepared query operands and the
+ * per-wave partial top-k lists live in `workspace` (device) of
  * tq_workspace_bytes(TQ_OP_TOPK, ...) bytes, 256-byte aligned (TQ_ERR_WORKSPACE
  * otherwise). TQ_ERR_UNSUPPORTED for a layout whose operands exceed 150 KiB of LDS
  * per row of four queries. */
