@@ -129,6 +129,23 @@ def test_workspace_sizes(tq):
     assert q.workspace_bytes(tq.TQ_OP_SCORE, 1, 100, 4) == 0
 
 
+def test_search_key_chunks_stay_within_a_32bit_byte_range(tq):
+    """The search kernel reads a work-group's key chunk through one buffer resource (a
+    32-bit byte range), so the plan must split a bank into chunks of at most 2 GiB of bit
+    words. The top-k workspace beyond the query operands (two partial lists of k entries per
+    wave, 8 waves per work-group, per chunk) gives the chunk count the plan chose."""
+    v = _with_fake_ptrs(tq, d=768, m=768, groups=((768, 3),))  # 96 words = 384 B per key
+    G, k = 8192, 10  # 1024 query blocks: on its own the plan would keep one chunk per bank
+    per_chunk = 2 * G * 8 * k * 4
+    for n, want in ((1_000_000, 1), (4_000_000, 1), (6_000_000, 2), (12_000_000, 3)):
+        extra = v.workspace_bytes(tq.TQ_OP_TOPK, 1, n, G, k) - v.workspace_bytes(tq.TQ_OP_SCORE, 1, n, G)
+        assert extra % per_chunk == 0
+        kc = extra // per_chunk
+        chunk_tiles = -(-(-(-n // 16)) // kc)
+        assert chunk_tiles * 96 * 64 <= 2**31 - 1, (n, kc)
+        assert kc == want, (n, kc)
+
+
 def _rc(fn, *a):
     return fn(*a)
 
