@@ -97,10 +97,8 @@ enum { TQ_APPEND_PREPARED = 1 };
  *   norm_dtype   storage of the bank's norm arrays: TQ_F32 (0), or TQ_F16 for the
  *                16-bit norm format variant (turboquant-pytorch write-up, results: the
  *                compressed cache size it reports at 3 bits is met with 16-bit norms).
- *                TQ_F16 requires d <= 128 and m <= 128 (TQ_ERR_UNSUPPORTED otherwise,
- *                from every entry point); tq_encode and tq_encode_append then need
- *                16-byte aligned bits (tq_encode) and keys 16-byte (f32) or 8-byte
- *                (bf16) aligned, else TQ_ERR_UNSUPPORTED. Other values: TQ_ERR_ARG. */
+ *                Every encoder writes it and every reader takes it, for all layouts.
+ *                Other values: TQ_ERR_ARG. */
 typedef struct {
     int32_t d, m, n_groups;
     int32_t group_dim[2];

@@ -33,7 +33,7 @@ struct EncArgs {
     float cent[2][16];
     float thr[2][15];
     double sqrt_d[2];
-    int nh;  // 1: the bank stores binary16 norms (encode_split_kernel only)
+    int nh;  // 1: the bank stores binary16 norms
 };
 
 // S'[i][pos] for pos = goff[g] + j: sum_k S[i][chan[goff[g]+k]] * R_g[j][k] (fp64 sums in
@@ -112,8 +112,8 @@ template <typename KT>
 __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys, long n, int n_tiles,
                                                      const float *__restrict__ rot, const float *__restrict__ sp,
                                                      const int *__restrict__ chan, EncArgs a,
-                                                     uint32_t *__restrict__ bits, float *__restrict__ norms,
-                                                     float *__restrict__ rnorms, EncSlots slots) {
+                                                     uint32_t *__restrict__ bits, void *__restrict__ norms,
+                                                     void *__restrict__ rnorms, EncSlots slots) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float s_inv[ENC_KEYS][2], s_coef[ENC_KEYS][2], s_cent[2][16];
     const int d = a.d, m = a.m, ld = d + 2;
@@ -159,11 +159,20 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
             s = wave_sum_f64(s);
             if (lane == 0) {
                 const double nu = sqrt(s);
-                const float nu_s = (float)nu;
+                // stored norm (float32 or its binary16 rounding) for the reconstruction
+                const float nu_f = (float)nu;
+                const uint16_t nu_h = f32_to_binary16(nu_f);
+                const float nu_s = a.nh ? norm_f32(nu_h) : nu_f;
                 s_inv[i][g] = nu > 0.0 ? (float)(a.sqrt_d[g] / nu) : 0.0f;
                 s_coef[i][g] = (float)((double)nu_s / a.sqrt_d[g]);
                 const long sl = slot_of(i);
-                if (sl >= 0) norms[((size_t)bank * out_pad + sl) * a.ng + g] = nu_s;
+                if (sl >= 0) {
+                    const size_t at = ((size_t)bank * out_pad + sl) * a.ng + g;
+                    if (a.nh)
+                        static_cast<uint16_t *>(norms)[at] = nu_h;
+                    else
+                        static_cast<float *>(norms)[at] = nu_f;
+                }
             }
         }
     }
@@ -218,7 +227,14 @@ __global__ __launch_bounds__(256) void encode_kernel(const KT *__restrict__ keys
         s = wave_sum_f64(s);
         const long sl = slot_of(i);
         // the MSE-only quantiser (m = 0) stores no residual norm: 0
-        if (lane == 0 && sl >= 0) rnorms[(size_t)bank * out_pad + sl] = m > 0 ? (float)sqrt(s) : 0.0f;
+        if (lane == 0 && sl >= 0) {
+            const size_t at = (size_t)bank * out_pad + sl;
+            const float rv = m > 0 ? (float)sqrt(s) : 0.0f;
+            if (a.nh)
+                static_cast<uint16_t *>(rnorms)[at] = f32_to_binary16(rv);
+            else
+                static_cast<float *>(rnorms)[at] = rv;
+        }
     }
 
     // 4. stage 2 on MFMA: P = U S'^T, sign = [P >= 0]

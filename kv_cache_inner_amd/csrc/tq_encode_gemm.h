@@ -139,7 +139,7 @@ template <typename KT>
 __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     const KT *__restrict__ keys, const int *__restrict__ chan, const uint16_t *__restrict__ rp3, EncArgs a, int g,
     long t0, int rows, int n_tiles, long n, int jbase, float *__restrict__ U, float *__restrict__ rho_part,
-    uint32_t *__restrict__ bits, float *__restrict__ norms) {
+    uint32_t *__restrict__ bits, void *__restrict__ norms) {
     constexpr int XP = sizeof(KT) == 2 ? 1 : 3;
     __shared__ __align__(16) u32x4 As[2][3][8][64];
     __shared__ __align__(16) u32x4 Bs[2][XP][8][64];
@@ -235,10 +235,20 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     nsq += __shfl_xor(nsq, 2, 64);
     if (sk == 0) {
         const double nu = sqrt(nsq);
-        const float nu_s = (float)nu;
+        // the stored norm (float32, or its binary16 rounding): the reconstruction, and so
+        // the residual, use it; the rotated coordinates use the unrounded norm
+        const float nu_f = (float)nu;
+        const uint16_t nu_h = f32_to_binary16(nu_f);
+        const float nu_s = a.nh ? norm_f32(nu_h) : nu_f;
         s_inv[srow] = nu > 0.0 ? (float)(a.sqrt_d[g] / nu) : 0.0f;
         s_coef[srow] = (float)((double)nu_s / a.sqrt_d[g]);
-        if (tile == 0 && kbase + srow < rows) norms[((size_t)br.tile * 16 + (srow & 15)) * ng + g] = nu_s;
+        if (tile == 0 && kbase + srow < rows) {
+            const size_t at = ((size_t)br.tile * 16 + (srow & 15)) * ng + g;
+            if (a.nh)
+                static_cast<uint16_t *>(norms)[at] = nu_h;
+            else
+                static_cast<float *>(norms)[at] = nu_f;
+        }
     }
     float th[7];
 #pragma unroll
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_prj_kernel(const float *_
                                                                   long t0, int rows, int J,
                                                                   const float *__restrict__ rho_part,
                                                                   uint32_t *__restrict__ bits,
-                                                                  float *__restrict__ rnorms) {
+                                                                  void *__restrict__ rnorms) {
     __shared__ __align__(16) u32x4 As[2][3][8][64];
     __shared__ __align__(16) u32x4 Bs[2][3][8][64];
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, i = lane & 15;
@@ -397,7 +407,12 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_prj_kernel(const float *_
         if (kl < rows) {
             double s = 0.0;
             for (int j = 0; j < J; ++j) s += (double)rho_part[(size_t)j * EG_CHUNK + kl];
-            rnorms[(size_t)(t0 + (kl >> 4)) * 16 + (kl & 15)] = (float)sqrt(s);
+            const size_t at = (size_t)(t0 + (kl >> 4)) * 16 + (kl & 15);
+            const float rv = (float)sqrt(s);
+            if (a.nh)
+                static_cast<uint16_t *>(rnorms)[at] = f32_to_binary16(rv);
+            else
+                static_cast<float *>(rnorms)[at] = rv;
         }
     }
 }

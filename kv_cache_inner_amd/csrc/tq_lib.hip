@@ -255,8 +255,6 @@ static int check_params(const tq_params *p) {
     if (!p->rot || (p->m > 0 && !p->proj)) return TQ_ERR_ARG;
     if (misaligned16(p->rot) || misaligned16(p->proj)) return TQ_ERR_ARG;  // read as 16-byte rows
     if (p->norm_dtype != TQ_F32 && p->norm_dtype != TQ_F16) return TQ_ERR_ARG;
-    // binary16 norms: written by the d, m <= 128 encoder, read by the kernels of those layouts
-    if (p->norm_dtype == TQ_F16 && (p->d > 128 || p->m > 128)) return TQ_ERR_UNSUPPORTED;
     return TQ_OK;
 }
 
@@ -315,18 +313,13 @@ static int with_layout(const tq_params *p, F &&f) {
 }
 
 // As with_layout, for the kernels that read a bank's norms: the layout as stored, wrapped
-// in HalfNorms for the 16-bit norm format (which the encoder writes for d, m <= 128 only).
+// in HalfNorms for the 16-bit norm format.
 template <class F>
 static int with_bank_layout(const tq_params *p, F &&f) {
     const bool h = half_norms(p);
     return with_layout(p, [&](auto l) -> int {
-        using L = decltype(l);
-        if constexpr (L::D <= ENCS_DMAX && L::M <= ENCS_DMAX) {
-            if (h) return f(HalfNorms<L>{});
-            return f(l);
-        } else {
-            return h ? (int)TQ_ERR_UNSUPPORTED : (int)f(l);
-        }
+        if (h) return f(HalfNorms<decltype(l)>{});
+        return f(l);
     });
 }
 
@@ -500,11 +493,9 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (p->m == 0 && enc_large(p)) return TQ_ERR_UNSUPPORTED;  // MSE-only keys up to 128 dimensions
     const int64_t n_tiles = (n + 15) / 16;
     if (banks * n_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
-    // d, m <= 128 with aligned words: the persistent bf16-split encoder (the only one that
-    // writes binary16 norms)
+    // d, m <= 128 with aligned words: the persistent bf16-split encoder
     const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)out->bits % 16) == 0 &&
                        ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
-    if (half_norms(p) && !split) return TQ_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     const EncArgs a = enc_args(p);
     float *sp = (float *)workspace;
@@ -549,18 +540,18 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
                 if (dtype == TQ_F32)
                     hipLaunchKernelGGL(enc_gemm_rot_kernel<float>, grid, dim3(EG_THREADS), 0, st, (const float *)keys,
                                        p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles, (long)n, jbase,
-                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, (float *)out->norms);
+                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, out->norms);
                 else
                     hipLaunchKernelGGL(enc_gemm_rot_kernel<uint16_t>, grid, dim3(EG_THREADS), 0, st,
                                        (const uint16_t *)keys, p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles,
                                        (long)n, jbase, (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits,
-                                       (float *)out->norms);
+                                       out->norms);
                 jbase += 2 * ntile;
             }
             const dim3 pgrid((unsigned)(kblocks * ((p->m + EG_TILE - 1) / EG_TILE)));
             hipLaunchKernelGGL(enc_gemm_prj_kernel, pgrid, dim3(EG_THREADS), 0, st, (const float *)(ws + ew.U),
                                (const uint16_t *)(ws + ew.s3), a, (long)tc, rows, ew.J, (const float *)(ws + ew.rho),
-                               out->bits, (float *)out->rnorms);
+                               out->bits, out->rnorms);
             if ((rc = launch_status())) return rc;
         }
         return TQ_OK;
@@ -571,13 +562,13 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
     if (dtype == TQ_F32) {
         (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)n, (int)n_tiles,
-                           p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms, (float *)out->rnorms,
+                           p->rot, sp, p->group_chan, a, out->bits, out->norms, out->rnorms,
                            EncSlots{nullptr, 0});
     } else {
         (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)n,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
-                           (float *)out->rnorms, EncSlots{nullptr, 0});
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms,
+                           out->rnorms, EncSlots{nullptr, 0});
     }
     return launch_status();
 }
@@ -593,8 +584,6 @@ static int check_append(const tq_params *p, const void *keys, int dtype, int64_t
     const int64_t n_tiles = (count + 15) / 16, cap_tiles = (n_cap + 15) / 16;
     if (banks * n_tiles > INT32_MAX || cap_tiles > INT32_MAX) return TQ_ERR_UNSUPPORTED;
     if (enc_smem_bytes(p->d, p->m) > 150 * 1024) return TQ_ERR_UNSUPPORTED;
-    const bool split = p->d <= ENCS_DMAX && p->m <= ENCS_DMAX && ((uintptr_t)keys % (dtype == TQ_F32 ? 16 : 8)) == 0;
-    if (half_norms(p) && !split) return TQ_ERR_UNSUPPORTED;  // binary16 norms: the split encoder only
     return TQ_OK;
 }
 
@@ -631,13 +620,13 @@ static int launch_append(const tq_params *p, const void *keys, int dtype, int64_
     if (dtype == TQ_F32) {
         (void)hipFuncSetAttribute((const void *)encode_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<float>, grid, dim3(256), smem, st, (const float *)keys, (long)count,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
-                           (float *)out->rnorms, slots);
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms,
+                           out->rnorms, slots);
     } else {
         (void)hipFuncSetAttribute((const void *)encode_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         hipLaunchKernelGGL(encode_kernel<uint16_t>, grid, dim3(256), smem, st, (const uint16_t *)keys, (long)count,
-                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, (float *)out->norms,
-                           (float *)out->rnorms, slots);
+                           (int)n_tiles, p->rot, sp, p->group_chan, a, out->bits, out->norms,
+                           out->rnorms, slots);
     }
     return launch_status();
 }

@@ -188,3 +188,101 @@ def test_half_norm_full_decode8b_layer_sampled(tq):
         qi = g.integers(0, cfg.G, len(ki))
         ref = oracle.score_pairs(orc, rb[b], rn[b], rr[b], q[b], qi, ki)
         check_scores(got[b, qi, ki], ref, f"bank {b}")
+
+
+# ------------------------------------------------------------------------------------------
+# keys above 128 dimensions (the two-GEMM encoder and the large-operand readers) and key rows
+# at unaligned addresses (the tile-per-work-group encoder), with binary16 norms
+# ------------------------------------------------------------------------------------------
+
+def _cfg_with(base, **kw):
+    import dataclasses
+
+    return dataclasses.replace(workloads.CONFIGS[base], **kw)
+
+
+def _encode_check(tq, cfg, bits, x, unaligned=False):
+    import torch
+
+    gpu, orc = both_params(cfg, bits, norm16=True)
+    banks, n = x.shape[0], x.shape[1]
+    bank = tq.Bank(gpu, banks, n)
+    t = _dev(cfg, x)
+    if unaligned:  # the same values one element off a 16-byte boundary
+        flat = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        flat[1:] = t.reshape(-1)
+        t = flat[1:].view(t.shape)
+    tq.tq_encode(gpu, t, bank)
+    torch.cuda.synchronize()
+    gb = download_bank(bank)
+    assert bank.norms.dtype == torch.float16 and bank.rnorms.dtype == torch.float16
+    rep = {}
+    for b in range(banks):
+        check_encode((gb[0][b], gb[1][b], gb[2][b]), oracle.encode_trace(orc, x[b]), orc, n, rep)
+    return rep
+
+
+@pytest.mark.parametrize("case", ["search_b4", "search_b2", "d256_two_groups_bf16", "m256_bf16"])
+def test_half_norm_encode_large_keys(tq, case):
+    """The two-GEMM encoder writes binary16 norms, its residual taken against the rounded
+    norm: d = 768 fp32 unit vectors (search), two permuted channel groups at d = 256 with
+    a partial row tile, and m above 128 at d = 128."""
+    if case.startswith("search"):
+        cfg, bits, n = workloads.CONFIGS["search"], int(case[-1]), 301
+    elif case == "d256_two_groups_bf16":
+        groups = ((64, 3), (192, 2))
+        cfg, bits, n = _cfg_with("longctx", d=256, m=160, key_dtype="bf16", cfg_id=81, outliers=64,
+                                 groups=groups), 3, 1100
+    else:
+        cfg, bits, n = _cfg_with("decode8b", d=128, m=256, key_dtype="bf16", cfg_id=82), 3, 1100
+    say(f"half-norm encode, large keys: {case} d={cfg.d} m={cfg.m} n={n}")
+    x = workloads.keys(cfg, n=n, banks=[0] if cfg.banks == 1 else [0, 1])
+    say("   report", _encode_check(tq, cfg, bits, x))
+
+
+@pytest.mark.parametrize("name,bits", [("decode3b", 3), ("search", 4)])
+def test_half_norm_encode_unaligned_keys(tq, name, bits):
+    """Key rows off a 16-byte boundary take the tile-per-work-group encoder, which writes
+    binary16 norms as well (d = 128 and d = 768)."""
+    cfg = workloads.CONFIGS[name]
+    n = 333 if name == "search" else 1000
+    say(f"half-norm encode, unaligned keys: {name} b={bits} n={n}")
+    x = workloads.keys(cfg, n=n, banks=[0])
+    say("   report", _encode_check(tq, cfg, bits, x, unaligned=True))
+
+
+@pytest.mark.parametrize("bits,n,G,k", [(4, 3003, 37, 10), (2, 2001, 9, 10), (4, 700, 3, 64)])
+def test_half_norm_search_readers(tq, bits, n, G, k):
+    """Top-k and scores (prepared operands in LDS; G <= 16 through the register-operand
+    scorer) of 768-dimensional keys with binary16 norms, on oracle-encoded bytes."""
+    import torch
+
+    cfg = workloads.CONFIGS["search"]
+    say(f"half-norm search readers: b={bits} n={n} G={G} k={k}")
+    gpu, orc = both_params(cfg, bits, norm16=True)
+    x = workloads.keys(cfg, n=n)
+    q = workloads.queries(cfg, G=G)
+    kb = _encode_banks(orc, x)
+    bank = upload_bank(tq, gpu, kb[0], kb[1], kb[2], n)
+    qd = torch.from_numpy(q).cuda()
+    ref = oracle.score(orc, kb[0][0], kb[1][0], kb[2][0], n, q[0])
+    vals, idx = tq.tq_topk(gpu, bank, qd, k)
+    check_topk(vals.cpu().numpy()[0], idx.cpu().numpy()[0], ref, k)
+    check_scores(tq.tq_score(gpu, bank, qd).cpu().numpy()[0], ref, "scores")
+
+
+@pytest.mark.parametrize("G", [4, 20])
+def test_half_norm_scores_d256(tq, G):
+    import torch
+
+    cfg = _cfg_with("decode8b", d=256, m=256, key_dtype="bf16", cfg_id=83)
+    n = 1234
+    say(f"half-norm scores d=256 G={G}")
+    gpu, orc = both_params(cfg, 3, norm16=True)
+    x = workloads.keys(cfg, n=n, banks=[0, 1])
+    q = workloads.queries(cfg, banks=[0, 1], G=G)
+    kb = _encode_banks(orc, x)
+    bank = upload_bank(tq, gpu, kb[0], kb[1], kb[2], n)
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda()).cpu().numpy()
+    for b in range(2):
+        check_scores(got[b], oracle.score(orc, kb[0][b], kb[1][b], kb[2][b], n, q[b]), f"bank {b}")

@@ -103,6 +103,8 @@ def test_bank_geometry(tq, groups, m, W, bpk):
 @pytest.mark.parametrize("groups,m,W,bpk", [
     (((128, 2),), 128, 12, 52),        # d=128, b=3 with binary16 norms: 4 bytes fewer per key
     (((32, 2), (96, 1)), 128, 9, 42),  # two groups: two norms and the residual norm, 2 bytes each
+    (((256, 2),), 256, 24, 100),       # keys above 128 dimensions (the two-GEMM encoder)
+    (((768, 3),), 768, 96, 388),       # the search layout at b = 4
 ])
 def test_bank_geometry_with_half_norms(tq, groups, m, W, bpk):
     d = sum(g[0] for g in groups)
@@ -280,24 +282,11 @@ def test_argument_validation_returns_before_any_launch(tq):
     assert L.tq_topk(good.ref, ctypes.byref(oddbank), 1, 100, 0x1000, 4, 10, 0x2000, 0x3000, 0x4000, 1 << 20,
                      None) == tq.TQ_ERR_ARG
     assert att(keys=ctypes.byref(oddbank)) == tq.TQ_ERR_ARG
-    # the 16-bit norm format: other norm types are invalid; above d, m = 128 and for keys
-    # the split encoder cannot read it is unsupported, before anything is enqueued
+    # the 16-bit norm format: other norm types are invalid
     for nd in (tq.TQ_BF16, 3, -1):
         bad = patched(norm_dtype=nd)
         assert L.tq_bank_layout(bad.ref, 10, None, None, None) == tq.TQ_ERR_ARG
         assert L.tq_encode(bad.ref, 0x1000, 0, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20, None) == tq.TQ_ERR_ARG
-    big = _with_fake_ptrs(tq, d=256, m=256, groups=((256, 2),))
-    big.struct.norm_dtype = tq.TQ_F16
-    assert L.tq_bank_layout(big.ref, 10, None, None, None) == tq.TQ_ERR_UNSUPPORTED
-    assert L.tq_score(big.ref, ctypes.byref(bank), 1, 10, 0x1000, 4, 0x2000, 0x3000, 1 << 20,
-                      None) == tq.TQ_ERR_UNSUPPORTED
-    h = patched(norm_dtype=tq.TQ_F16)
-    assert L.tq_encode(h.ref, 0x1004, tq.TQ_F32, 1, 10, ctypes.byref(bank), 0x2000, 1 << 20,
-                       None) == tq.TQ_ERR_UNSUPPORTED
-    assert L.tq_encode(h.ref, 0x1000, tq.TQ_F32, 1, 10, ctypes.byref(tq.tq_bank(0x30004, 0x40000, 0x50000)),
-                       0x2000, 1 << 20, None) == tq.TQ_ERR_UNSUPPORTED
-    assert A(h.ref, 0x1002, tq.TQ_BF16, 1, 1, 0x6000, 100, ctypes.byref(bank), 0, 0x2000, 1 << 20,
-             None) == tq.TQ_ERR_UNSUPPORTED
     # empty inputs are valid no-ops
     assert L.tq_encode(good.ref, None, 0, 0, 10, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
     assert L.tq_encode(good.ref, None, 0, 3, 0, ctypes.byref(nullbank), None, 0, None) == tq.TQ_OK
