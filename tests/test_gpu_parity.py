@@ -168,6 +168,33 @@ def test_score_ring_steady_state_every_output(tq, offset):
         check_scores(got[b], oracle.score(orc, rb[b], rn[b], rr[b], n, q[b]), f"bank {b}")
 
 
+@pytest.mark.parametrize("case", ["b3_one_wg", "b3_four_wgs", "b3_offset", "b4_one_wg", "longctx_one_wg"])
+def test_score_ring_full_runs_every_output(tq, case):
+    """Work-group runs of whole tiles (every key below n, 16 waves with equal runs):
+    256 banks x 4096 keys (one work-group per bank) and 64 banks x 16384 keys (four per
+    bank), at b = 3 (grouped 16-byte stores; offset: the per-tile stores), b = 4 (3-tile
+    ring halves) and two channel groups; random bank bytes, every score against the
+    oracle."""
+    import torch
+
+    name = "longctx" if case.startswith("longctx") else "decode8b"
+    cfg = workloads.CONFIGS[name]
+    bits = 4 if case.startswith("b4") else 3
+    banks, n = (64, 16384) if case == "b3_four_wgs" else (256, 4096)
+    offset = 1 if case == "b3_offset" else 0
+    gpu, orc = both_params(cfg, bits)
+    W, npad, _ = gpu.layout(n)
+    rb, rn, rr = workloads.random_bank(cfg.cfg_id, banks, npad, W, len(orc.spec.groups), layer=6)
+    bank = upload_bank(tq, gpu, rb, rn, rr, n)
+    q = np.random.default_rng(12).standard_normal((banks, 4, cfg.d)).astype(np.float32)
+    flat = torch.full((banks * 4 * n + offset,), float("nan"), dtype=torch.float32, device="cuda")
+    scores = flat[offset:].view(banks, 4, n)
+    say(f"ring full runs: {case}: {banks} x {n}, b={bits}, score offset {offset}")
+    got = tq.tq_score(gpu, bank, torch.from_numpy(q).cuda(), scores=scores).cpu().numpy()
+    for b in range(banks):
+        check_scores(got[b], oracle.score(orc, rb[b], rn[b], rr[b], n, q[b]), f"bank {b}")
+
+
 # ------------------------------------------------------------------------------------------
 # encoder against the oracle's encoding of the same keys
 # ------------------------------------------------------------------------------------------
