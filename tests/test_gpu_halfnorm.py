@@ -253,8 +253,9 @@ def test_half_norm_encode_unaligned_keys(tq, name, bits):
 
 @pytest.mark.parametrize("bits,n,G,k", [(4, 3003, 37, 10), (2, 2001, 9, 10), (4, 700, 3, 64)])
 def test_half_norm_search_readers(tq, bits, n, G, k):
-    """Top-k and scores (prepared operands in LDS; G <= 16 through the register-operand
-    scorer) of 768-dimensional keys with binary16 norms, on oracle-encoded bytes."""
+    """Top-k, scores (prepared operands in LDS; G <= 16 through the register-operand
+    scorer) and decompression of 768-dimensional keys with binary16 norms, on
+    oracle-encoded bytes."""
     import torch
 
     cfg = workloads.CONFIGS["search"]
@@ -269,6 +270,13 @@ def test_half_norm_search_readers(tq, bits, n, G, k):
     vals, idx = tq.tq_topk(gpu, bank, qd, k)
     check_topk(vals.cpu().numpy()[0], idx.cpu().numpy()[0], ref, k)
     check_scores(tq.tq_score(gpu, bank, qd).cpu().numpy()[0], ref, "scores")
+    # decompression of the same bytes, within the fp32 decoder's rounding bound
+    dec = tq.tq_decode(gpu, bank).cpu().numpy()[0]
+    v = oracle.decode(orc, kb[0][0], kb[1][0], n)
+    cb = 1 << (bits - 1)
+    tol = 4 * cfg.d * 2.0 ** -24 * kb[1][0][:n, :1].astype(np.float64) / np.sqrt(cfg.d) * \
+        np.abs(orc.rots[0]).sum(axis=0)[None] * np.abs(orc.cent[0, :cb]).max()
+    assert (np.abs(dec - v) <= tol).all()
 
 
 @pytest.mark.parametrize("G", [4, 20])
