@@ -405,16 +405,17 @@ def test_longctx_full_size_sampled(tq):
 # streaming append: keys encoded into chosen slots of preallocated banks
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("unaligned", [False, True])
-def test_encode_append_slots(tq, unaligned):
+@pytest.mark.parametrize("name,unaligned", [("longctx", False), ("longctx", True), ("search", False)])
+def test_encode_append_slots(tq, name, unaligned):
     """Appends in three calls at different per-bank positions (not multiples of 16), one of
     them running past the capacity; appended slots match the oracle's encoding of their keys
     and every other slot keeps its previous bytes. Unaligned key rows take the
-    tile-per-block encoder, aligned ones the persistent one."""
+    tile-per-block encoder, aligned ones the persistent one; 768-dimensional vectors (new
+    rows of a search database, b = 4) take the tile-per-block encoder."""
     import torch
 
-    cfg = workloads.CONFIGS["longctx"]
-    gpu, orc = both_params(cfg, 3)
+    cfg = workloads.CONFIGS[name]
+    gpu, orc = both_params(cfg, 4 if name == "search" else 3)
     n_cap, banks = 100, 2
     keys = workloads.keys(cfg, n=64, banks=[2, 3])
     bank = tq.Bank(gpu, banks, n_cap)
@@ -429,9 +430,11 @@ def test_encode_append_slots(tq, unaligned):
         pos = start + k0
         if k0 == 38:
             pos[1] = n_cap - 7  # bank 1: only 7 of these 26 keys fit (the rest are skipped)
-        kk = torch.from_numpy(np.ascontiguousarray(keys[:, k0:k1])).cuda().to(torch.bfloat16)
+        kk = torch.from_numpy(np.ascontiguousarray(keys[:, k0:k1])).cuda()
+        if cfg.key_dtype == "bf16":
+            kk = kk.to(torch.bfloat16)
         if unaligned:  # the same values at an address that is not a multiple of 8 bytes
-            flat = torch.zeros(kk.numel() + 1, dtype=torch.bfloat16, device="cuda")
+            flat = torch.zeros(kk.numel() + 1, dtype=kk.dtype, device="cuda")
             flat[1:] = kk.reshape(-1)
             kk = flat[1:].view(kk.shape)
         say(f"append keys [{k0}, {k1}) at slots {pos.tolist()}")
