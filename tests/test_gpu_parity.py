@@ -99,6 +99,45 @@ def test_score_longctx_two_groups(tq):
     say("max err", _score_check(tq, cfg, 3, keys, q))
 
 
+@pytest.mark.parametrize("G", [1, 3, 8, 16, 20])
+def test_score_longctx_two_groups_other_G(tq, G):
+    """Two permuted channel groups at query counts other than the ring scorer's four: the
+    fused scorers (G = 1..16, operands in registers) and prepared operands in LDS (G = 20),
+    on a ragged bank length."""
+    cfg = workloads.CONFIGS["longctx"]
+    say(f"score longctx two groups: 2 banks x 1500, G={G}")
+    keys = workloads.keys(cfg, n=1500, banks=[2, 5])
+    q = workloads.queries(cfg, banks=[2, 5], G=G)
+    say("max err", _score_check(tq, cfg, 3, keys, q))
+
+
+@pytest.mark.parametrize("name,bits,G", [("decode8b", 3, 4), ("decode3b", 4, 7), ("longctx", 3, 5), ("search", 4, 9)])
+def test_prepared_operands_reused(tq, name, bits, G):
+    """The split scorer's public pair: tq_prepare_queries once, then tq_score_prepared on
+    two different sets of banks with the same operands (they depend on the queries and the
+    parameters only); both against the oracle."""
+    import torch
+
+    cfg = workloads.CONFIGS[name]
+    n = 700 if name == "search" else 1200
+    banks = [0] if name == "search" else [0, 1]
+    gpu, orc = both_params(cfg, bits)
+    q = workloads.queries(cfg, banks=banks, G=G)
+    qd = torch.from_numpy(q).cuda()
+    say(f"prepared operands: {name} b={bits} G={G} n={n}")
+    ws = torch.empty(gpu.workspace_bytes(tq.TQ_OP_SCORE, len(banks), n, G), dtype=torch.uint8, device="cuda")
+    tq.tq_prepare_queries(gpu, qd, ws)
+    for layer in (0, 1):
+        keys = workloads.keys(cfg, layer=layer, n=n, banks=banks)
+        refs = [oracle.encode(orc, keys[b]) for b in range(len(banks))]
+        bank = upload_bank(tq, gpu, np.stack([r[0] for r in refs]), np.stack([r[1] for r in refs]),
+                           np.stack([r[2] for r in refs]), n)
+        scores = torch.full((len(banks), G, n), float("nan"), dtype=torch.float32, device="cuda")
+        got = tq.tq_score_prepared(gpu, bank, G, ws, scores).cpu().numpy()
+        for b in range(len(banks)):
+            check_scores(got[b], oracle.score(orc, *refs[b], n, q[b]), f"keys of layer {layer}, bank {b}")
+
+
 @pytest.mark.parametrize("n,G", [(1, 1), (15, 3), (16, 4), (17, 5), (33, 16), (1000, 2), (999, 13)])
 def test_score_ragged_shapes(tq, n, G):
     cfg = workloads.CONFIGS["decode8b"]
