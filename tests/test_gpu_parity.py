@@ -267,18 +267,23 @@ def test_encode_ragged(tq, n):
     _encode_check(tq, cfg, 4, workloads.keys(cfg, n=n, banks=[3, 4, 5]))
 
 
-def test_encode_degenerate_keys(tq):
-    """Zero keys, a key zero in one channel group only, and very large / small norms."""
-    cfg = workloads.CONFIGS["longctx"]
+@pytest.mark.parametrize("name", ["longctx", "search"])
+def test_encode_degenerate_keys(tq, name):
+    """Zero keys, a key zero in one channel group only, and very large / small norms; the
+    search shape (d = 768) takes the two-GEMM encoder."""
+    cfg = workloads.CONFIGS[name]
     keys = workloads.keys(cfg, n=64, banks=[0])
     keys[0, 3] = 0.0
-    chan = workloads.group_channels(cfg)
-    keys[0, 5, chan[:32]] = 0.0
-    keys[0, 6, chan[32:]] = 0.0
+    if name == "longctx":
+        chan = workloads.group_channels(cfg)
+        keys[0, 5, chan[:32]] = 0.0
+        keys[0, 6, chan[32:]] = 0.0
+    else:
+        keys[0, 5, :400] = 0.0
     keys[0, 7] *= 1024.0
     keys[0, 8] /= 1024.0
-    say("encode degenerate keys")
-    gpu, orc, bank, _ = _encode_check(tq, cfg, 3, keys)
+    say(f"encode degenerate keys: {name}")
+    gpu, orc, bank, _ = _encode_check(tq, cfg, 3 if name == "longctx" else 4, keys)
     _, _, rr = download_bank(bank)
     assert rr[0, 3] == 0.0
 
