@@ -510,7 +510,12 @@ __device__ __forceinline__ int encs_elem(int pos, int key) {
     return ((((pos >> 5) << 6) + (((pos >> 3) & 3) << 4) + key) << 3) + (pos & 7);
 }
 
-template <typename KT>
+// NGT: the channel-group count when fixed at compile time (2: the compiler drops the
+// one-group paths and the per-lane group masks leave the scalar registers), 0: read from
+// the arguments. Measured: fixing two groups made the long-context encoder about 7 % faster
+// (byte-identical banks); fixing one group made the single-group encoder about 10 % slower
+// (a vector register spilled), so single-group layouts keep the run-time count.
+template <typename KT, int NGT>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
@@ -528,7 +533,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, q = lane >> 4;
-    const int D = a.d, M = a.m, ng = a.ng;
+    const int D = a.d, M = a.m, ng = NGT ? NGT : a.ng;
     const int grid = gridDim.x;
     const bool rot_role = wv < ENCS_ROT;
 

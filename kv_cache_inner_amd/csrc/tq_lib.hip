@@ -508,11 +508,11 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
         const int64_t total = banks * n_tiles;
         const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
         if (dtype == TQ_F32)
-            hipLaunchKernelGGL(encode_split_kernel<float>, pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<float, 2> : encode_split_kernel<float, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
                                (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits, out->norms,
                                out->rnorms, EncSlots{nullptr, 0});
         else
-            hipLaunchKernelGGL(encode_split_kernel<uint16_t>, pgrid, dim3(ENCS_WAVES * 64), 0, st,
+            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<uint16_t, 2> : encode_split_kernel<uint16_t, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st,
                                (const uint16_t *)keys, (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan,
                                a, out->bits, out->norms, out->rnorms, EncSlots{nullptr, 0});
         return launch_status();
@@ -607,11 +607,11 @@ static int launch_append(const tq_params *p, const void *keys, int dtype, int64_
         const int64_t total = banks * n_tiles;
         const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
         if (dtype == TQ_F32)
-            hipLaunchKernelGGL(encode_split_kernel<float>, pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<float, 2> : encode_split_kernel<float, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
                                (long)count, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits,
                                out->norms, out->rnorms, slots);
         else
-            hipLaunchKernelGGL(encode_split_kernel<uint16_t>, pgrid, dim3(ENCS_WAVES * 64), 0, st,
+            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<uint16_t, 2> : encode_split_kernel<uint16_t, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st,
                                (const uint16_t *)keys, (long)count, (int)n_tiles, (int)total, p->rot, sp,
                                p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
         return launch_status();
