@@ -76,8 +76,9 @@ constexpr int AT_WAIT_VM0 = (7 << 4) | (15 << 8);
 // word's stored planes for all tiles of the chunk, then the logits and norms of its
 // query; one wait covers them all, so a work-group costs one memory round trip and the
 // products run from LDS.
-// NH: the value bank stores binary16 norms.
-template <int NG, bool NH>
+// NH: the value bank stores binary16 norms. GB: the code width of a one-group value bank
+// fixed at compile time (0: read from the arguments).
+template <int NG, bool NH, int GB>
 __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     const float *__restrict__ scores, const uint32_t *__restrict__ vbits, const void *__restrict__ vnorms, long n,
     int n_tiles, int G, int chunks, float scale, const int32_t *__restrict__ lengths, AttnArgs a,
@@ -105,7 +106,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_chunk_kernel(
     const int nwords = a.d >> 5;
     const bool wlive = wv < nwords;
     const int g = (NG > 1 && 32 * wv >= a.gdim[0]) ? 1 : 0;
-    const int gb = a.gbits[g];
+    static_assert(GB == 0 || NG == 1, "a fixed code width needs one channel group");
+    const int gb = GB ? GB : a.gbits[g];
     const int pstride = a.gdim[g] >> 5;
     const int wbase = a.gword[g] + wv - (a.goff[g] >> 5);
     const uint32_t *vb = vbits + (size_t)bank * n_tiles * a.W * 16;

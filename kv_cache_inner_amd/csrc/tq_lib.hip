@@ -1054,10 +1054,13 @@ extern "C" int tq_attend(const tq_params *kp, const tq_bank *keys, const tq_para
         hipLaunchKernelGGL(kern, grid, dim3(AT_THREADS), 0, st, logits, values->bits, (const void *)values->norms,
                            (long)n, (int)n_tiles, (int)G, (int)chunks, scale, lengths, a, part);
     };
-    if (vp->n_groups == 1)
-        half_norms(vp) ? chunk_kernel(attn_chunk_kernel<1, true>) : chunk_kernel(attn_chunk_kernel<1, false>);
+    const bool nh = half_norms(vp);
+    if (vp->n_groups == 2)
+        nh ? chunk_kernel(attn_chunk_kernel<2, true, 0>) : chunk_kernel(attn_chunk_kernel<2, false, 0>);
+    else if (vp->group_bits[0] == 3)
+        nh ? chunk_kernel(attn_chunk_kernel<1, true, 3>) : chunk_kernel(attn_chunk_kernel<1, false, 3>);
     else
-        half_norms(vp) ? chunk_kernel(attn_chunk_kernel<2, true>) : chunk_kernel(attn_chunk_kernel<2, false>);
+        nh ? chunk_kernel(attn_chunk_kernel<1, true, 0>) : chunk_kernel(attn_chunk_kernel<1, false, 0>);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(banks * G)), dim3(AT_MERGE_WAVES * 64), 0, st, part,
                        (int)chunks, vp->rot,
