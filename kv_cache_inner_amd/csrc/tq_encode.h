@@ -406,7 +406,7 @@ __device__ __forceinline__ void encr_bucket(const f32x4 &acc, float inv, float c
             below += sw[t] >> 31;
         }
         const uint32_t idx = NT - below;
-        u[r] = y - coef * cent[idx];
+        u[r] = fmaf(-coef, cent[idx], y);  // one rounding, whatever the compiler contracts
         // bit p of the bucket, from the sign words (bucket = number of thresholds <= z)
         uint32_t b0, b1 = 0, b2 = 0;
         if constexpr (NB == 1) {
@@ -510,12 +510,14 @@ __device__ __forceinline__ int encs_elem(int pos, int key) {
     return ((((pos >> 5) << 6) + (((pos >> 3) & 3) << 4) + key) << 3) + (pos & 7);
 }
 
-// NGT: the channel-group count when fixed at compile time (2: the compiler drops the
-// one-group paths and the per-lane group masks leave the scalar registers), 0: read from
-// the arguments. Measured: fixing two groups made the long-context encoder about 7 % faster
-// (byte-identical banks); fixing one group made the single-group encoder about 10 % slower
-// (a vector register spilled), so single-group layouts keep the run-time count.
-template <typename KT, int NGT>
+// NGT: the channel-group count fixed at compile time (0: read from the arguments); NBT: the
+// codebook width of a one-group layout fixed at compile time (0: read from the arguments).
+// Fixed counts let the compiler drop the unused paths, thresholds and per-lane group masks,
+// which otherwise spill scalar registers. Measured (in-process A/Bs): two groups about 7 %
+// faster on the long-context banks; one group with its width fixed 3.5 % (b = 3) and 7 %
+// (b = 4) faster on the decode shapes, where one group with the width left variable spilled
+// a vector register and was 10 % slower.
+template <typename KT, int NGT, int NBT = 0>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const int dg = g ? a.gdim[1] : a.gdim[0];
     const int off = g ? a.goff[1] : 0;
     const int j0 = pos0 - off, nkb_r = dg / 32;
-    const int nb = g ? a.gbits[1] : a.gbits[0];
+    const int nb = NBT ? NBT : (g ? a.gbits[1] : a.gbits[0]);
     float th[7];
 #pragma unroll
     for (int t = 0; t < 7; ++t) th[t] = t < (1 << nb) - 1 ? (g ? a.thr[1][t] : a.thr[0][t]) : INFINITY;

@@ -474,6 +474,18 @@ static EncArgs enc_args(const tq_params *p) {
     return a;
 }
 
+// The persistent encoder's instance for these parameters: compiled for two channel groups,
+// or for one group of a fixed codebook width.
+template <typename KT>
+static decltype(&encode_split_kernel<KT, 2>) split_encoder(const tq_params *p) {
+    if (p->n_groups == 2) return &encode_split_kernel<KT, 2>;
+    switch (p->group_bits[0]) {
+        case 1: return &encode_split_kernel<KT, 1, 1>;
+        case 2: return &encode_split_kernel<KT, 1, 2>;
+        default: return &encode_split_kernel<KT, 1, 3>;
+    }
+}
+
 static void launch_prep_proj(const tq_params *p, const EncArgs &a, float *sp, hipStream_t st) {
     if (p->m == 0) return;  // no sketch, no S'
     const int bx = p->d <= 64 ? 64 : (p->d <= 128 ? 128 : 256);
@@ -508,11 +520,11 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
         const int64_t total = banks * n_tiles;
         const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
         if (dtype == TQ_F32)
-            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<float, 2> : encode_split_kernel<float, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+            hipLaunchKernelGGL(split_encoder<float>(p), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
                                (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits, out->norms,
                                out->rnorms, EncSlots{nullptr, 0});
         else
-            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<uint16_t, 2> : encode_split_kernel<uint16_t, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st,
+            hipLaunchKernelGGL(split_encoder<uint16_t>(p), pgrid, dim3(ENCS_WAVES * 64), 0, st,
                                (const uint16_t *)keys, (long)n, (int)n_tiles, (int)total, p->rot, sp, p->group_chan,
                                a, out->bits, out->norms, out->rnorms, EncSlots{nullptr, 0});
         return launch_status();
@@ -607,11 +619,11 @@ static int launch_append(const tq_params *p, const void *keys, int dtype, int64_
         const int64_t total = banks * n_tiles;
         const dim3 pgrid((unsigned)std::min<int64_t>(total, std::max(cus, 1)));
         if (dtype == TQ_F32)
-            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<float, 2> : encode_split_kernel<float, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
+            hipLaunchKernelGGL(split_encoder<float>(p), pgrid, dim3(ENCS_WAVES * 64), 0, st, (const float *)keys,
                                (long)count, (int)n_tiles, (int)total, p->rot, sp, p->group_chan, a, out->bits,
                                out->norms, out->rnorms, slots);
         else
-            hipLaunchKernelGGL((p->n_groups == 2 ? encode_split_kernel<uint16_t, 2> : encode_split_kernel<uint16_t, 0>), pgrid, dim3(ENCS_WAVES * 64), 0, st,
+            hipLaunchKernelGGL(split_encoder<uint16_t>(p), pgrid, dim3(ENCS_WAVES * 64), 0, st,
                                (const uint16_t *)keys, (long)count, (int)n_tiles, (int)total, p->rot, sp,
                                p->group_chan, a, out->bits, out->norms, out->rnorms, slots);
         return launch_status();
