@@ -543,7 +543,7 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
         const int64_t total = banks * n_tiles;
         for (int64_t tc = 0; tc < total; tc += EG_CHUNK / 16) {
             const int rows = (int)std::min<int64_t>(EG_CHUNK, (total - tc) * 16);
-            const int kblocks = (rows + EG_TILE - 1) / EG_TILE;
+            const int kblocks = (rows + EG_KT - 1) / EG_KT;
             int jbase = 0;
             for (int g = 0; g < p->n_groups; ++g) {
                 const int ntile = (p->group_dim[g] + EG_TILE - 1) / EG_TILE;
