@@ -238,14 +238,16 @@ def test_score_ring_full_runs_every_output(tq, case):
 # encoder against the oracle's encoding of the same keys
 # ------------------------------------------------------------------------------------------
 
-def test_encode_tiny_full(tq):
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_tiny_full(tq, bits):
+    """fp32 keys at every codebook width the encoder is compiled for (1, 2, 3 bits + sketch)."""
     cfg = workloads.CONFIGS["tiny"]
-    say("encode tiny")
-    _, _, _, rep = _encode_check(tq, cfg, 3, workloads.keys(cfg))
+    say(f"encode tiny b={bits}")
+    _, _, _, rep = _encode_check(tq, cfg, bits, workloads.keys(cfg))
     say("report", rep)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_encode_decode3b_full(tq, bits):
     cfg = workloads.CONFIGS["decode3b"]
     say(f"encode decode3b b={bits}")
