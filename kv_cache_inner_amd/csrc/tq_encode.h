@@ -511,13 +511,15 @@ __device__ __forceinline__ int encs_elem(int pos, int key) {
 }
 
 // NGT: the channel-group count fixed at compile time (0: read from the arguments); NBT: the
-// codebook width of a one-group layout fixed at compile time (0: read from the arguments).
-// Fixed counts let the compiler drop the unused paths, thresholds and per-lane group masks,
-// which otherwise spill scalar registers. Measured (in-process A/Bs): two groups about 7 %
-// faster on the long-context banks; one group with its width fixed 3.5 % (b = 3) and 7 %
-// (b = 4) faster on the decode shapes, where one group with the width left variable spilled
-// a vector register and was 10 % slower.
-template <typename KT, int NGT, int NBT = 0>
+// codebook width of a one-group layout fixed at compile time (0: read from the arguments);
+// DT: d = m fixed at compile time (0: read from the arguments). Fixed values let the compiler
+// drop the unused paths, thresholds and per-lane group masks (which otherwise spill scalar
+// registers) and turn the K-block counts and operand offsets into constants. Measured
+// (in-process A/Bs, byte-identical banks): two groups about 7 % faster on the long-context
+// banks; one group with its width fixed 3.5 % (b = 3) and 7 % (b = 4) faster on the decode
+// shapes (one group with the width left variable spilled a vector register and was 10 %
+// slower); d = m = 128 fixed on top of that, another 14 % (b = 3) and 16 % (b = 4).
+template <typename KT, int NGT, int NBT = 0, int DT = 0>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, q = lane >> 4;
-    const int D = a.d, M = a.m, ng = NGT ? NGT : a.ng;
+    const int D = DT ? DT : a.d, M = DT ? DT : a.m, ng = NGT ? NGT : a.ng;
     const int grid = gridDim.x;
     const bool rot_role = wv < ENCS_ROT;
 
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const int pos0 = 16 * wv;
     const bool rot_live = rot_role && pos0 < D;
     const int g = (ng > 1 && pos0 >= a.gdim[0]) ? 1 : 0;
-    const int dg = g ? a.gdim[1] : a.gdim[0];
+    const int dg = (DT && NGT == 1) ? DT : (g ? a.gdim[1] : a.gdim[0]);
     const int off = g ? a.goff[1] : 0;
     const int j0 = pos0 - off, nkb_r = dg / 32;
     const int nb = NBT ? NBT : (g ? a.gbits[1] : a.gbits[0]);

@@ -475,10 +475,19 @@ static EncArgs enc_args(const tq_params *p) {
 }
 
 // The persistent encoder's instance for these parameters: compiled for two channel groups,
-// or for one group of a fixed codebook width.
+// or for one group of a fixed codebook width; for d = m = 128 (the KV-cache head size) also
+// for that size.
 template <typename KT>
 static decltype(&encode_split_kernel<KT, 2>) split_encoder(const tq_params *p) {
-    if (p->n_groups == 2) return &encode_split_kernel<KT, 2>;
+    const bool d128 = p->d == 128 && p->m == 128;
+    if (p->n_groups == 2) return d128 ? &encode_split_kernel<KT, 2, 0, 128> : &encode_split_kernel<KT, 2>;
+    if (d128) {
+        switch (p->group_bits[0]) {
+            case 1: return &encode_split_kernel<KT, 1, 1, 128>;
+            case 2: return &encode_split_kernel<KT, 1, 2, 128>;
+            default: return &encode_split_kernel<KT, 1, 3, 128>;
+        }
+    }
     switch (p->group_bits[0]) {
         case 1: return &encode_split_kernel<KT, 1, 1>;
         case 2: return &encode_split_kernel<KT, 1, 2>;
