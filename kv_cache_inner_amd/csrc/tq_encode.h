@@ -512,14 +512,14 @@ __device__ __forceinline__ int encs_elem(int pos, int key) {
 
 // NGT: the channel-group count fixed at compile time (0: read from the arguments); NBT: the
 // codebook width of a one-group layout fixed at compile time (0: read from the arguments);
-// DT: d = m fixed at compile time (0: read from the arguments). Fixed values let the compiler
+// DT, MT: d and m fixed at compile time (DT = 0: both read from the arguments). Fixed values let the compiler
 // drop the unused paths, thresholds and per-lane group masks (which otherwise spill scalar
 // registers) and turn the K-block counts and operand offsets into constants. Measured
 // (in-process A/Bs, byte-identical banks): two groups about 7 % faster on the long-context
 // banks; one group with its width fixed 3.5 % (b = 3) and 7 % (b = 4) faster on the decode
 // shapes (one group with the width left variable spilled a vector register and was 10 %
 // slower); d = m = 128 fixed on top of that, another 14 % (b = 3) and 16 % (b = 4).
-template <typename KT, int NGT, int NBT = 0, int DT = 0>
+template <typename KT, int NGT, int NBT = 0, int DT = 0, int MT = DT>
 __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const KT *__restrict__ keys, long n, int n_tiles, int total_tiles, const float *__restrict__ rot,
     const float *__restrict__ sp, const int *__restrict__ chan, EncArgs a, uint32_t *__restrict__ bits,
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(ENCS_WAVES * 64) void encode_split_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, q = lane >> 4;
-    const int D = DT ? DT : a.d, M = DT ? DT : a.m, ng = NGT ? NGT : a.ng;
+    const int D = DT ? DT : a.d, M = DT ? MT : a.m, ng = NGT ? NGT : a.ng;
     const int grid = gridDim.x;
     const bool rot_role = wv < ENCS_ROT;
 

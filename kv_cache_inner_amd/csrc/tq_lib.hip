@@ -476,7 +476,7 @@ static EncArgs enc_args(const tq_params *p) {
 
 // The persistent encoder's instance for these parameters: compiled for two channel groups,
 // or for one group of a fixed codebook width; for d = m = 128 (the KV-cache head size) also
-// for that size.
+// for that size, and for 3-bit value banks (d = 128, m = 0).
 template <typename KT>
 static decltype(&encode_split_kernel<KT, 2>) split_encoder(const tq_params *p) {
     const bool d128 = p->d == 128 && p->m == 128;
@@ -488,6 +488,8 @@ static decltype(&encode_split_kernel<KT, 2>) split_encoder(const tq_params *p) {
             default: return &encode_split_kernel<KT, 1, 3, 128>;
         }
     }
+    if (p->d == 128 && p->m == 0 && p->group_bits[0] == 3)  // 3-bit MSE-only value banks
+        return &encode_split_kernel<KT, 1, 3, 128, 0>;
     switch (p->group_bits[0]) {
         case 1: return &encode_split_kernel<KT, 1, 1>;
         case 2: return &encode_split_kernel<KT, 1, 2>;
