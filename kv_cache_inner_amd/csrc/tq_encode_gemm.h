@@ -134,8 +134,9 @@ __device__ __forceinline__ void eg_load_a(const uint16_t *__restrict__ ap, long 
 // ---- stage 1: rotation of group g, buckets, code words, residual chunk, |u|^2 partials
 // Work-group tile: 128 coordinates x EG_KT = 256 keys; wave w owns coordinates 64 (w & 1)..
 // and keys 64 (w >> 1).. (4 x 4 MFMA blocks of 16 x 16): each fragment read from LDS feeds
-// four MFMAs.
-template <typename KT>
+// four MFMAs. DT: the dimension of a one-group layout with d = m fixed at compile time (0: read
+// from the arguments); the d = m = 768 instance encodes search keys about 5 % faster, bytes unchanged.
+template <typename KT, int DT = 0>
 __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     const KT *__restrict__ keys, const int *__restrict__ chan, const uint16_t *__restrict__ rp3, EncArgs a, int g,
     long t0, int rows, int n_tiles, long n, int jbase, float *__restrict__ U, float *__restrict__ rho_part,
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     __shared__ float s_cent[8];
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, i = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wv & 1, wk = wv >> 1;
-    const int dg = a.gdim[g], off = a.goff[g], D = a.d, ng = a.ng, nb = a.gbits[g];
+    const int dg = DT ? DT : a.gdim[g], off = DT ? 0 : a.goff[g], D = DT ? DT : a.d, ng = DT ? 1 : a.ng;
+    const int nb = a.gbits[g];
     const int ntile = (dg + EG_TILE - 1) / EG_TILE;
     int kblock, tile;
     eg_block(ntile, kblock, tile);
@@ -320,7 +322,8 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     }
 }
 
-// ---- stage 2: projection of the residual chunk, sign words, residual norms
+// ---- stage 2: projection of the residual chunk, sign words, residual norms (DT as in stage 1)
+template <int DT = 0>
 __global__ __launch_bounds__(EG_THREADS) void enc_gemm_prj_kernel(const float *__restrict__ U,
                                                                   const uint16_t *__restrict__ sp3, EncArgs a,
                                                                   long t0, int rows, int J,
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_prj_kernel(const float *_
     __shared__ __align__(16) u32x4 Bs[2][3][16][64];
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, i = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), wr = wv & 1, wk = wv >> 1;
-    const int D = a.d, M = a.m;
+    const int D = DT ? DT : a.d, M = DT ? DT : a.m;
     const int ntile = (M + EG_TILE - 1) / EG_TILE;
     int kblock, tile;
     eg_block(ntile, kblock, tile);

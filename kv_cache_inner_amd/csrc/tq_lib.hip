@@ -552,6 +552,7 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
                            tot, (uint16_t *)(ws + ew.s3));
         if ((rc = launch_status())) return rc;
         const int64_t total = banks * n_tiles;
+        const bool d768 = p->n_groups == 1 && p->d == 768 && p->m == 768;  // the search geometry
         for (int64_t tc = 0; tc < total; tc += EG_CHUNK / 16) {
             const int rows = (int)std::min<int64_t>(EG_CHUNK, (total - tc) * 16);
             const int kblocks = (rows + EG_KT - 1) / EG_KT;
@@ -561,20 +562,21 @@ extern "C" int tq_encode(const tq_params *p, const void *keys, int dtype, int64_
                 const dim3 grid((unsigned)(kblocks * ntile));
                 const uint16_t *r3 = (const uint16_t *)(ws + ew.r3[g]);
                 if (dtype == TQ_F32)
-                    hipLaunchKernelGGL(enc_gemm_rot_kernel<float>, grid, dim3(EG_THREADS), 0, st, (const float *)keys,
-                                       p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles, (long)n, jbase,
-                                       (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits, out->norms);
+                    hipLaunchKernelGGL((d768 ? enc_gemm_rot_kernel<float, 768> : enc_gemm_rot_kernel<float, 0>), grid,
+                                       dim3(EG_THREADS), 0, st, (const float *)keys, p->group_chan, r3, a, g, (long)tc,
+                                       rows, (int)n_tiles, (long)n, jbase, (float *)(ws + ew.U),
+                                       (float *)(ws + ew.rho), out->bits, out->norms);
                 else
-                    hipLaunchKernelGGL(enc_gemm_rot_kernel<uint16_t>, grid, dim3(EG_THREADS), 0, st,
+                    hipLaunchKernelGGL((enc_gemm_rot_kernel<uint16_t, 0>), grid, dim3(EG_THREADS), 0, st,
                                        (const uint16_t *)keys, p->group_chan, r3, a, g, (long)tc, rows, (int)n_tiles,
                                        (long)n, jbase, (float *)(ws + ew.U), (float *)(ws + ew.rho), out->bits,
                                        out->norms);
                 jbase += 2 * ntile;
             }
             const dim3 pgrid((unsigned)(kblocks * ((p->m + EG_TILE - 1) / EG_TILE)));
-            hipLaunchKernelGGL(enc_gemm_prj_kernel, pgrid, dim3(EG_THREADS), 0, st, (const float *)(ws + ew.U),
-                               (const uint16_t *)(ws + ew.s3), a, (long)tc, rows, ew.J, (const float *)(ws + ew.rho),
-                               out->bits, out->rnorms);
+            hipLaunchKernelGGL((d768 ? enc_gemm_prj_kernel<768> : enc_gemm_prj_kernel<0>), pgrid, dim3(EG_THREADS), 0,
+                               st, (const float *)(ws + ew.U), (const uint16_t *)(ws + ew.s3), a, (long)tc, rows,
+                               ew.J, (const float *)(ws + ew.rho), out->bits, out->rnorms);
             if ((rc = launch_status())) return rc;
         }
         return TQ_OK;
