@@ -63,6 +63,14 @@ constexpr bool lds_fits() {
 // the current step's MFMAs run (one MFMA, then two of the next step's vector instructions).
 constexpr int LDS_LA = 8;
 
+// Streamed batches with two row tiles run on v_mfma_i32_32x32x32_i8 (LDS_WIDE), with
+// LDS_WIDE_VALU vector instructions scheduled after each MFMA. Measured at d = 768, b = 4
+// (1024 queries, 2M keys): 20.6-20.8 ms against 21.3-21.6 for the 16 x 16 x 64 form, the
+// same lists; 4 or 9 instructions per MFMA, a lookahead of 5 or 12 quads, or separate
+// accumulators per K half (four chains instead of two) measured no faster.
+constexpr bool LDS_WIDE = true;
+constexpr int LDS_WIDE_VALU = 6;
+
 template <class L>
 struct StreamOrder {
     struct Table {
@@ -153,6 +161,35 @@ __device__ __forceinline__ void topk_offer4(float (&lv)[4], int (&li)[4], float 
     }
 }
 
+// Offers the estimates of a 32-key pair to two queries of a row tile: lanes 0..31 hold
+// query Q0's (lists lv[Q0]), lanes 32..63 query Q0 + 1's; every lane keeps its own query's
+// k-th entry in (tv, ti). Otherwise as topk_offer4.
+template <int Q0>
+__device__ __forceinline__ void topk_offer_pair(float (&lv)[4], int (&li)[4], float &tv, int &ti, float est, int key,
+                                                bool ok, int kh, int k, int lane) {
+    uint64_t m = __ballot(ok && topk_better(est, key, tv, ti));
+    if (!m) return;
+    while (m) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1;
+        const float v = __shfl(est, src, 64);
+        const int id = __shfl(key, src, 64);
+        if (src < 32)
+            topk_insert(lv[Q0], li[Q0], v, id, lane);
+        else
+            topk_insert(lv[Q0 + 1], li[Q0 + 1], v, id, lane);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float t = __shfl(lv[Q0 + h], k - 1, 64);
+        const int i = __shfl(li[Q0 + h], k - 1, 64);
+        if (kh == h) {
+            tv = t;
+            ti = i;
+        }
+    }
+}
+
 template <class L, int RQ, bool TOPK>
 __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
     const uint32_t *__restrict__ bits, const typename L::NormT *__restrict__ norms,
@@ -204,6 +241,7 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
     const long n_pad = (long)n_tiles * 16;
     constexpr int TB = lds_tb<L>();
     constexpr bool DB = lds_db<L>();
+    constexpr bool WIDE = !DB && TB == 4 && RQ == 2 && LDS_WIDE;
     TileStream<L, 1, TB> ts{bits + (size_t)bank * n_tiles * L::W * 16, norms + (size_t)bank * n_pad * L::NG,
                            rnorms + (size_t)bank * n_pad, nullptr, n, G, t0, t1};
     ts.init_lane();
@@ -302,7 +340,7 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
         finish(t, A.nu, A.rho, acc);
         A = B;
     }
-    } else {
+    } else if constexpr (!WIDE) {
     // streamed batches: stored quad sq of tile u in kw[sq][u] (the next batch's first quads
     // in kn until the batch ends)
     using SO = StreamOrder<L>;
@@ -443,6 +481,209 @@ __global__ __launch_bounds__(LDS_WAVES * 64) void score_lds_kernel(
                 for (int u = 0; u < TB; ++u) kw[sq][u] = kn[sq][u];
             }
         });
+    }
+    } else {
+    // 32 x 32 x 32 form of the streamed batches (four key tiles, two row tiles): the two row
+    // tiles are the 32 rows of one v_mfma_i32_32x32x32_i8 and a pair of key tiles its 32
+    // columns, so a step issues half as many MFMAs for the same multiply-adds, and each one
+    // leaves the issue port free for more of the vector work (about six instructions per
+    // MFMA instead of two). Lane (n, kh) = (lane & 31, lane >> 5) holds key j of tile
+    // 2 p + hi of the batch (hi = n >> 4; pairs p = 0, 1) and, of each quad, stored words
+    // 4 sq + 2 w + kh for w = 0, 1 (the two 32-deep halves of the quad's K step); the
+    // operand fragments are the same LDS bytes read at other lane offsets (row tile hi,
+    // row j, word 2 w + kh). Its accumulator registers 4 a .. 4 a + 3 hold the four limbs of
+    // query 2 a + kh of the eight (row tile a / 2, query 2 (a % 2) + kh in it).
+    using SO = StreamOrder<L>;
+    static_assert(L::NQ >= LDS_LA, "the lookahead spans at most one batch");
+    constexpr int NSTEP = 2 * L::NQ;
+    const int kh = lane >> 5, hi = (lane >> 4) & 1;
+    const uint32_t *bbank = bits + (size_t)bank * n_tiles * L::W * 16;
+    const typename L::NormT *nbank = norms + (size_t)bank * n_pad * L::NG;
+    const typename L::NormT *rbank = rnorms + (size_t)bank * n_pad;
+    const __amdgpu_buffer_rsrc_t chunk_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(bbank) + (size_t)c0 * (L::W * 16), 0, (c1 - c0) * (L::W * 64), BUF_DWORD3);
+    // byte offset of word kh of this lane's key in pair p of the batch at tile tb (tiles past
+    // the run clamped to its last: their keys are never offered or stored)
+    auto pair_off = [&](int tb, int p) { return (min(tb + 2 * p + hi, t1 - 1) - c0) * (L::W * 64) + 4 * (16 * kh + j); };
+    // stored quad sq: word 4 sq + 2 w + kh of pair p in dst[2 p + w]
+    auto load_sq = [&](uint32_t (&dst)[4], auto sqc, const int (&vo)[2]) {
+        constexpr int sq = decltype(sqc)::value;
+        static_for<2>([&](auto wc) {
+            constexpr int w = decltype(wc)::value;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                if constexpr (4 * sq + 2 * w + 1 < L::W) {
+                    dst[2 * p + w] = __builtin_amdgcn_raw_buffer_load_b32(chunk_rs, vo[p] + 128 * w, 256 * sq, 0);
+                } else if constexpr (4 * sq + 2 * w < L::W) {
+                    // word 2 w + 1 is past the key's words: lanes kh = 1 read word 4 sq instead
+                    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(chunk_rs, kh ? vo[p] - 64 : vo[p] + 128 * w,
+                                                                            256 * sq, 0);
+                    dst[2 * p + w] = kh ? 0u : v;
+                } else {
+                    dst[2 * p + w] = 0u;
+                }
+            }
+        });
+    };
+    // the thresholds (k-th entries) of this lane's four queries
+    float tw[4];
+    int tiw[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        tw[a] = -INFINITY;
+        tiw[a] = INT32_MAX;
+    }
+    // the per-query constants with the terms' scales folded in, as the other paths form them
+    __shared__ double csf[4 * RQ][L::NCLS][2];
+    for (int e = tid; e < 4 * RQ * L::NCLS * 2; e += LDS_WAVES * 64) {
+        const int c = (e / 2) % L::NCLS;
+        const double f = c < L::NG ? (c == 0 ? sc.inv_sqrt_d[0] : sc.inv_sqrt_d[1]) : sc.qjl;
+        (&csf[0][0][0])[e] = (&cst[0][0][0])[e] * f;
+    }
+    __syncthreads();
+    auto finish_w = [&](int t, const float (&nu)[2][L::NG], const float (&rho)[2], i32x16 (&acc)[2][L::NCLS]) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int tile = t + 2 * p + hi;
+            const long key = (long)tile * 16 + j;
+            const bool key_live = tile < t1 && key < n;
+            static_for<4>([&](auto ac) {
+                constexpr int a = decltype(ac)::value;
+                const int qi = 2 * a + kh;  // query of the eight
+                double est = 0.0;
+                static_for<L::NCLS>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    constexpr int g = c < L::NG ? c : 0;
+                    const double s = c < L::NG ? (double)nu[p][g] : (double)rho[p];
+                    const i32x4 lm{acc[p][c][4 * a], acc[p][c][4 * a + 1], acc[p][c][4 * a + 2], acc[p][c][4 * a + 3]};
+                    est = fma(s, fma(limbs_to_f64<L::class_positions(c)>(lm), csf[qi][c][0], csf[qi][c][1]), est);
+                });
+                const float e = (float)est;
+                const int gq = 4 * rt0 + qi;
+                if constexpr (TOPK) {
+                    topk_offer_pair<2 * (a % 2)>(lv[a / 2], li[a / 2], tw[a], tiw[a], e, (int)key, key_live && gq < G,
+                                                 kh, k, lane);
+                } else {
+                    if (key_live && gq < G) ob[(size_t)gq * n + key] = e;
+                }
+            });
+        }
+    };
+    int vo[2], vn[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) vo[p] = pair_off(t0, p);
+    uint32_t kw[L::NSQ][4];
+    static_for<L::NSQ>([&](auto sc) {
+        constexpr int sq = decltype(sc)::value;
+        if constexpr (SO::first_use(sq) < LDS_LA)
+            if (t0 < t1) load_sq(kw[sq], sc, vo);
+    });
+    for (int t = t0; t < t1; t += TB) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) vn[p] = pair_off(t + TB, p);
+        float nu[2][L::NG], rho[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int tile = min(t + 2 * p + hi, t1 - 1);
+#pragma unroll
+            for (int g = 0; g < L::NG; ++g) nu[p][g] = norm_f32(nbank[(size_t)tile * (16 * L::NG) + j * L::NG + g]);
+            rho[p] = norm_f32(rbank[(size_t)tile * 16 + j]);
+        }
+        uint32_t kn[L::NSQ][4];
+        i32x16 acc[2][L::NCLS];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int c = 0; c < L::NCLS; ++c) acc[p][c] = i32x16{};
+        auto der_of = [&](auto ic, uint32_t (&der)[4]) {
+            constexpr int q = SO::at(decltype(ic)::value);
+            constexpr int nx = L::quad_nx(q);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                der[x] = kw[L::quad_sq(q, 0)][x];
+                if constexpr (nx > 1) der[x] ^= kw[L::quad_sq(q, 1)][x];
+                if constexpr (nx > 2) der[x] ^= kw[L::quad_sq(q, 2)][x];
+            }
+        };
+        auto frags_of = [&](auto sc, i8x16 (&a)[L::NCLS][2]) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int q = SO::at(s / 2), h = s % 2;
+            static_for<L::NCLS>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if constexpr (L::quad_has(q, c)) {
+#pragma unroll
+                    for (int w = 0; w < 2; ++w)
+                        a[c][w] = *reinterpret_cast<const i8x16 *>(&fa[hi][L::frag_index(q, h, c)][16 * (2 * w + kh) + j][0]);
+                }
+            });
+        };
+        uint32_t der[4];
+        i8x16 bk[4], ak[L::NCLS][2];
+        der_of(std::integral_constant<int, 0>{}, der);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) bk[x] = expand_half<0>(der[x]);
+        frags_of(std::integral_constant<int, 0>{}, ak);
+        static_for<NSTEP>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int i = s / 2, h = s % 2;
+            constexpr int q = SO::at(i);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (h == 0) {
+                static_for<L::NSQ>([&](auto qc) {
+                    constexpr int sq = decltype(qc)::value;
+                    constexpr int fu = SO::first_use(sq);
+                    if constexpr (fu < L::NQ && fu == i + LDS_LA) load_sq(kw[sq], qc, vo);
+                    if constexpr (fu < LDS_LA && fu == i + LDS_LA - L::NQ) load_sq(kn[sq], qc, vn);
+                });
+            }
+            i8x16 bn[4], an[L::NCLS][2];
+            if constexpr (s + 1 < NSTEP) {
+                if constexpr (h == 1) der_of(std::integral_constant<int, i + 1>{}, der);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) bn[x] = expand_half<(s + 1) % 2>(der[x]);
+                frags_of(std::integral_constant<int, s + 1>{}, an);
+            }
+            constexpr int nmf = [] {
+                int m = 0;
+                for (int c = 0; c < L::NCLS; ++c) m += L::quad_has(q, c) ? 4 : 0;
+                return m;
+            }();
+            static_for<L::NCLS>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if constexpr (L::quad_has(q, c)) {
+#pragma unroll
+                    for (int w = 0; w < 2; ++w)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            acc[p][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ak[c][w], bk[2 * p + w], acc[p][c], 0, 0, 0);
+                }
+            });
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            static_for<nmf>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, LDS_WIDE_VALU, 0);
+            });
+            if constexpr (s + 1 < NSTEP) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) bk[x] = bn[x];
+                static_for<L::NCLS>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) ak[c][w] = an[c][w];
+                });
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        finish_w(t, nu, rho, acc);
+        static_for<L::NSQ>([&](auto sc) {
+            constexpr int sq = decltype(sc)::value;
+            if constexpr (SO::first_use(sq) < LDS_LA) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) kw[sq][x] = kn[sq][x];
+            }
+        });
+#pragma unroll
+        for (int p = 0; p < 2; ++p) vo[p] = vn[p];
     }
     }
     if constexpr (TOPK) {
