@@ -19,6 +19,8 @@
 
 namespace tq {
 
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));  // a 32 x 32 MFMA accumulator
+
 // Each operand fragment read from LDS (1 KiB per wave) feeds the MFMAs of lds_tb() key tiles,
 // and each expanded key operand the MFMAs of lds_rows() row tiles. Per MFMA the CU's LDS
 // (128 B/clk) and vector ALU (4 ops per 16-cycle MFMA per SIMD) are then loaded with 1 KiB /
