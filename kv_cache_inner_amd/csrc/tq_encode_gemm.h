@@ -67,6 +67,13 @@ __device__ __forceinline__ void eg_block(int ntile, int &kblock, int &tile) {
     kblock = logical / ntile;
 }
 
+// Slot of (row r of a 16-row block, K slot sk) in the block's 64 16-byte operand slots: the
+// MFMA lane 16 sk + r, with bits 2-3 of r flipped by sk. Lane l reads slot l ^ (4 (l >> 4)),
+// a permutation inside each 16-lane group; the staging threads (four K slots of one row
+// in consecutive lanes) then write 16 distinct slots per 16 lanes instead of 4 each 256 B
+// apart.
+__device__ __forceinline__ int eg_slot(int r, int sk) { return 16 * sk + ((r & 15) ^ (4 * sk)); }
+
 // Stores this thread's 8 values of a B row (split into XP pieces) at its operand slot.
 template <int XP, int NBLK = 8>
 __device__ __forceinline__ void eg_store_b(const float (&v)[8], u32x4 (*Bs)[NBLK][64], int srow, int sk) {
@@ -84,7 +91,7 @@ __device__ __forceinline__ void eg_store_b(const float (&v)[8], u32x4 (*Bs)[NBLK
         }
     }
 #pragma unroll
-    for (int p = 0; p < XP; ++p) Bs[p][srow >> 4][16 * sk + (srow & 15)] = pc[p];
+    for (int p = 0; p < XP; ++p) Bs[p][srow >> 4][eg_slot(srow, sk)] = pc[p];
 }
 
 // One K step of a wave's 4 x 4 MFMA blocks (64 rows x 64 keys) from the LDS operand buffers
@@ -93,16 +100,17 @@ __device__ __forceinline__ void eg_store_b(const float (&v)[8], u32x4 (*Bs)[NBLK
 template <int XP>
 __device__ __forceinline__ void eg_mma4(const u32x4 (*As)[8][64], const u32x4 (*Bs)[16][64], int wr, int wk, int lane,
                                         f32x4 (&acc)[4][4]) {
+    const int sl = lane ^ (4 * (lane >> 4));  // eg_slot of this lane's fragment
     u32x4 bf[4][XP];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int p = 0; p < XP; ++p) bf[kb][p] = Bs[p][4 * wk + kb][lane];
+        for (int p = 0; p < XP; ++p) bf[kb][p] = Bs[p][4 * wk + kb][sl];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         u32x4 af[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) af[p] = As[p][4 * wr + rb][lane];
+        for (int p = 0; p < 3; ++p) af[p] = As[p][4 * wr + rb][sl];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             f32x4 c = acc[rb][kb];
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_rot_kernel(
     };
     auto stage = [&](int buf, const u32x4 (&av)[3], const float (&bv)[2][8]) {
 #pragma unroll
-        for (int p = 0; p < 3; ++p) As[buf][p][srow >> 4][16 * sk + (srow & 15)] = av[p];
+        for (int p = 0; p < 3; ++p) As[buf][p][srow >> 4][eg_slot(srow, sk)] = av[p];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(EG_THREADS) void enc_gemm_prj_kernel(const float *_
 
     auto stage = [&](int buf, const u32x4 (&av)[3], const float (&bv)[2][8]) {
 #pragma unroll
-        for (int p = 0; p < 3; ++p) As[buf][p][srow >> 4][16 * sk + (srow & 15)] = av[p];
+        for (int p = 0; p < 3; ++p) As[buf][p][srow >> 4][eg_slot(srow, sk)] = av[p];
 #pragma unroll
         for (int h = 0; h < 2; ++h) eg_store_b<3, 16>(bv[h], Bs[buf], srow + 128 * h, sk);
     };
